@@ -1,0 +1,265 @@
+/*
+ * nomas_attn.h -- C ABI of the action-aware causal attention library (gfx950).
+ *
+ * The operation.  Hy-Nomas generates video segment by segment; each segment's
+ * keys and values join a permanent, growing cache that later segments attend
+ * to ("Tencent's Hy-Nomas Steers a 60-Second Video World ..." (gpts24.com),
+ * section "One World, Generated Segment by Segment").  Attention is joint over
+ * video and text tokens of 16 heads x 128 dims ("Summary (Overview)" page,
+ * Theoretical Foundation) and masked by these rules ("Summary (Overview)",
+ * Model Architecture: Segment-wise Causal Attention and Action-Aware Causal
+ * Attention, Figure 6b; onedev.kr review, section "무엇과 다른가"):
+ *   - a query of segment j sees segments 0..j of its own video (both ways
+ *     inside segment j, nothing later);
+ *   - every segment's descriptive head stays visible to later segments;
+ *   - an action tail a_k is visible only inside its own segment, to video
+ *     queries whose latent frame lies in a_k's window [lo, hi), and (text-query
+ *     reading "R") to a_k's own tokens;
+ *   - packed videos never see each other; padding is never visible.
+ * Hidden pairs get -inf logits; the library computes exact softmax attention
+ * O = softmax(scale * Q K^T + M) V (and its gradient for training packs).
+ * The unmasked-pair count A of a call is the "A_i" of the FLOPs-based packing
+ * estimate ("Summary (Overview)", Training Infrastructure, Eq. 6; xyznot.com
+ * guide, "Dağıtık Paketleme FLOP Tahmini").
+ *
+ * Token order inside a segment record (a convention of this library):
+ *   [video tokens, frame-major | head | a_0 | a_1 | ... | n_pad padding]
+ *
+ * Conventions for every call:
+ *   - every function returns a nomas_status and never aborts or throws; on
+ *     failure nomas_last_error() holds a thread-local description;
+ *   - Q, K, V, O, dO, dQ, dK, dV are bf16, token-major [tokens][heads][128]
+ *     with the 128 dims contiguous and a caller-given token stride (elements,
+ *     >= heads*128, multiple of 8); device pointers must be 16-byte aligned;
+ *   - LSE is fp32 [heads][queries] (natural log; -inf for a row that sees no
+ *     key);
+ *   - device work is enqueued on the caller's HIP stream (NULL = default
+ *     stream) and is not waited for;
+ *   - plans and caches are library-owned handles; K/V cache storage, outputs
+ *     and workspaces are caller-owned device memory.
+ * Objects are not safe for concurrent mutation; nomas_attn_fwd may be called
+ * concurrently with distinct outputs and workspaces.
+ */
+#ifndef NOMAS_ATTN_H
+#define NOMAS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NOMAS_MAX_ACTIONS 32
+#define NOMAS_HEAD_DIM 128
+
+typedef int32_t nomas_status;
+enum {
+  NOMAS_OK = 0,
+  NOMAS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or option        */
+  NOMAS_ERR_LAYOUT = 2,           /* malformed segment records               */
+  NOMAS_ERR_UNSUPPORTED = 3,      /* head_dim != 128, unsupported tile size  */
+  NOMAS_ERR_CAPACITY = 4,         /* cache append would exceed capacity      */
+  NOMAS_ERR_STALE_PLAN = 5,       /* cache changed since the plan was built  */
+  NOMAS_ERR_ALIGNMENT = 6,        /* pointer or stride misaligned            */
+  NOMAS_ERR_HIP = 7               /* HIP runtime or launch failure           */
+};
+
+/* One action tail: n_tokens text tokens, visible to the segment's video
+ * queries whose latent frame f satisfies frame_lo <= f < frame_hi. */
+typedef struct {
+  int32_t n_tokens;
+  int32_t frame_lo;
+  int32_t frame_hi;
+} nomas_action;
+
+/* One segment.  (video, index) identifies it: segments of one video see the
+ * segments of the same video with index <= their own.  Sizes:
+ * n_frames * tokens_per_frame video tokens (the latent grid of Eq. 1), n_head
+ * head tokens, the action tails, then n_pad padding tokens.  Requirements:
+ * video >= 0, index >= 0, all counts >= 0, at least one token,
+ * 0 <= n_actions <= 32, each action n_tokens >= 1 and
+ * 0 <= frame_lo < frame_hi <= n_frames. */
+typedef struct {
+  int32_t video;
+  int32_t index;
+  int32_t n_frames;
+  int32_t tokens_per_frame;
+  int32_t n_head;
+  int32_t n_actions;
+  int32_t n_pad;
+  int32_t reserved; /* set to 0 */
+  nomas_action actions[NOMAS_MAX_ACTIONS];
+} nomas_segment;
+
+/* Tokens of a list of segments, concatenated in order.  A (video, index)
+ * may appear at most once per layout; a segment named in both the query and
+ * the key layout must carry identical records. */
+typedef struct {
+  int32_t n_segments;
+  const nomas_segment* segments;
+} nomas_layout;
+
+/* What text (head / tail) queries see of action tails; the pages only state
+ * the rule for video queries.  R: a tail's tokens see that tail, heads see
+ * none.  K: no text query sees a tail.  H: as R, and heads also see every
+ * tail of their own segment. */
+enum { NOMAS_TEXT_QUERY_R = 0, NOMAS_TEXT_QUERY_K = 1, NOMAS_TEXT_QUERY_H = 2 };
+
+/* Plan flags. */
+enum {
+  NOMAS_PLAN_HOST_ONLY = 1 /* build host tables only (no device upload);
+                              such a plan cannot run nomas_attn_fwd/bwd */
+};
+
+typedef struct {
+  int32_t num_heads;       /* >= 1                                        */
+  int32_t head_dim;        /* must be 128                                 */
+  int32_t block_q;         /* 0 = 128; the kernels support 128            */
+  int32_t block_k;         /* 0 = 64; the kernels support 64              */
+  int32_t text_query_mode; /* NOMAS_TEXT_QUERY_*                          */
+  int32_t flags;           /* NOMAS_PLAN_*                                */
+  int32_t reserved0;       /* set to 0                                    */
+  int32_t reserved1;       /* set to 0                                    */
+} nomas_plan_opts;
+
+typedef struct nomas_plan nomas_plan;
+typedef struct nomas_kvcache nomas_kvcache;
+
+/* Tile classes as exported by nomas_plan_export_classes. */
+enum { NOMAS_TILE_EMPTY = 0, NOMAS_TILE_FULL = 1, NOMAS_TILE_PARTIAL = 2 };
+
+typedef struct {
+  int64_t n_queries;
+  int64_t n_keys;          /* cached + new                                 */
+  int64_t n_cached_keys;
+  int64_t n_q_tiles;
+  int64_t n_k_tiles;
+  int64_t n_empty_tiles;
+  int64_t n_full_tiles;
+  int64_t n_partial_tiles;
+  int64_t unmasked_pairs;  /* A: number of visible (query, key) pairs      */
+  int64_t executed_pairs;  /* pairs inside FULL + PARTIAL tiles (in range) */
+  double effective_flop;   /* forward: 4 * head_dim * num_heads * A        */
+  int32_t block_q;
+  int32_t block_k;
+  int32_t num_heads;
+  int32_t text_query_mode;
+} nomas_plan_info;
+
+/* --------------------------------------------------------------------------
+ * Plans
+ * ------------------------------------------------------------------------ */
+
+/* Build a plan for one attention call shape.
+ *   q       query tokens.
+ *   kv_new  key/value tokens passed to each call (k_new / v_new).
+ *   cache   NULL, or a KV cache whose committed segments precede kv_new in
+ *           key order: keys = cache tokens (in append order) ++ kv_new.
+ *           The plan remembers the cache's current contents; after an append
+ *           or truncate that changes them, calls return NOMAS_ERR_STALE_PLAN.
+ * Expands the records into per-token descriptors, classifies every
+ * block_q x block_k tile as EMPTY, FULL or PARTIAL, builds per-q-tile and
+ * per-k-tile lists of non-empty tiles and counts A, then (unless
+ * NOMAS_PLAN_HOST_ONLY) copies the tables to the current HIP device
+ * (synchronously).  *out is owned by the caller until nomas_plan_destroy.
+ * Errors: INVALID_ARGUMENT, LAYOUT, UNSUPPORTED, HIP. */
+nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
+                             const nomas_kvcache* cache,
+                             const nomas_plan_opts* opts, nomas_plan** out);
+
+nomas_status nomas_plan_get_info(const nomas_plan* plan, nomas_plan_info* info);
+
+/* Dense tile class map, row-major [n_q_tiles][n_k_tiles] of NOMAS_TILE_*.
+ * n must be >= n_q_tiles * n_k_tiles. */
+nomas_status nomas_plan_export_classes(const nomas_plan* plan, uint8_t* host_buf,
+                                       size_t n);
+
+nomas_status nomas_plan_destroy(nomas_plan* plan);
+
+/* --------------------------------------------------------------------------
+ * Forward
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace nomas_attn_fwd needs for this plan (may be 0). */
+nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* plan, size_t* bytes);
+
+/* O = softmax(scale * Q K^T + M) V for the plan's queries.
+ *   q, o          [n_queries][H][128], token strides q_stride / o_stride.
+ *   k_new, v_new  [n_new_keys][H][128], token stride kv_stride.
+ *   cache         the plan's cache (NULL iff the plan has none); its K/V
+ *                 buffers supply keys [0, n_cached_keys).
+ *   lse           NULL or fp32 [H][n_queries].
+ *   workspace     device memory of nomas_attn_fwd_workspace_size bytes
+ *                 (may be NULL when that size is 0).
+ * Errors: INVALID_ARGUMENT (host-only plan, missing pointer or workspace),
+ * STALE_PLAN, ALIGNMENT, HIP. */
+nomas_status nomas_attn_fwd(const nomas_plan* plan, const nomas_kvcache* cache,
+                            const void* q, int64_t q_stride,
+                            const void* k_new, const void* v_new, int64_t kv_stride,
+                            void* o, int64_t o_stride, float* lse, float scale,
+                            void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/* --------------------------------------------------------------------------
+ * Backward (plans without a cache: training packs)
+ * ------------------------------------------------------------------------ */
+
+nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* plan, size_t* bytes);
+
+/* Gradients of O = attention(Q, K, V) for upstream dO:
+ *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ *   dK = scale dS^T Q,
+ * with P recomputed from lse (which must come from nomas_attn_fwd on the same
+ * inputs).  q, o, d_o, dq share q_stride; k, v, dk, dv share kv_stride.
+ * dq, dk, dv are written (not accumulated), bf16.
+ * Errors: INVALID_ARGUMENT (plan with a cache, host-only plan, missing
+ * pointer or workspace), ALIGNMENT, HIP. */
+nomas_status nomas_attn_bwd(const nomas_plan* plan,
+                            const void* q, const void* k, const void* v,
+                            const void* o, const void* d_o, const float* lse,
+                            int64_t q_stride, int64_t kv_stride,
+                            void* dq, void* dk, void* dv, float scale,
+                            void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/* --------------------------------------------------------------------------
+ * KV cache ("One World, Generated Segment by Segment": each segment's K/V is
+ * appended to a permanent, growing cache)
+ * ------------------------------------------------------------------------ */
+
+/* k_buf / v_buf: caller-owned device memory, bf16 [heads][capacity][128]
+ * (head-major, so one head's keys are contiguous).  The handle (segment
+ * records, lengths) is library-owned. */
+nomas_status nomas_kvcache_create(int32_t heads, int32_t head_dim, int64_t capacity,
+                                  void* k_buf, void* v_buf, nomas_kvcache** out);
+
+/* Append one segment: its tokens' K/V are k_new / v_new [tokens][H][128]
+ * (token stride kv_stride) and are copied behind the cached tokens on
+ * hip_stream.  Over capacity: NOMAS_ERR_CAPACITY and nothing is written or
+ * recorded.  A segment already in the cache: NOMAS_ERR_LAYOUT. */
+nomas_status nomas_kvcache_append(nomas_kvcache* cache, const nomas_segment* seg,
+                                  const void* k_new, const void* v_new,
+                                  int64_t kv_stride, void* hip_stream);
+
+/* Drop segments so that n_segments remain (rollback).  Plans built when the
+ * cache held exactly those segments become valid again. */
+nomas_status nomas_kvcache_truncate(nomas_kvcache* cache, int32_t n_segments);
+
+nomas_status nomas_kvcache_reset(nomas_kvcache* cache);
+nomas_status nomas_kvcache_len(const nomas_kvcache* cache, int64_t* n_tokens,
+                               int32_t* n_segments);
+nomas_status nomas_kvcache_destroy(nomas_kvcache* cache);
+
+/* --------------------------------------------------------------------------
+ * Errors
+ * ------------------------------------------------------------------------ */
+
+const char* nomas_status_string(nomas_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* nomas_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NOMAS_ATTN_H */

@@ -1,0 +1,467 @@
+// C ABI of the library: argument checks, plan upload, cache bookkeeping and
+// kernel launches.  Every entry point returns a status and records a
+// thread-local error text; nothing throws across the boundary.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "nomas_attn.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string t_err;
+
+nomas_status fail(nomas_status s, const std::string& what) {
+  t_err = what;
+  return s;
+}
+
+nomas_status ok() {
+  t_err.clear();
+  return NOMAS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint64_t next_cache_id() {
+  static uint64_t id = 0;
+  return __atomic_add_fetch(&id, 1, __ATOMIC_RELAXED);
+}
+
+}  // namespace
+
+struct nomas_kvcache {
+  int32_t heads = 0, head_dim = 0;
+  int64_t capacity = 0, len = 0;
+  void* k = nullptr;
+  void* v = nullptr;
+  std::vector<nomas_segment> segs;
+  std::vector<uint64_t> serials;   // unique per appended segment
+  uint64_t next_serial = 1;
+  uint64_t id = 0;
+};
+
+struct nomas_plan {
+  nomas::HostPlan host;
+  bool has_cache = false;
+  uint64_t cache_id = 0;
+  int32_t cache_nseg = 0;
+  uint64_t cache_last_serial = 0;
+  bool on_device = false;
+  int device = -1;
+  void* dmem = nullptr;
+  const nomas::QDescDev* d_qdesc = nullptr;
+  const nomas::KDescDev* d_kdesc = nullptr;
+  const int32_t *d_csr_ptr = nullptr, *d_csr_idx = nullptr;
+  const int32_t *d_csc_ptr = nullptr, *d_csc_idx = nullptr;
+};
+
+namespace {
+
+nomas_status check_layout_ptr(const nomas_layout* l, const char* name) {
+  if (!l) return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " layout is NULL");
+  if (l->n_segments < 0) return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + ": n_segments < 0");
+  if (l->n_segments > 0 && !l->segments)
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + ": segments is NULL");
+  return NOMAS_OK;
+}
+
+std::vector<nomas_segment> to_vec(const nomas_layout* l) {
+  return std::vector<nomas_segment>(l->segments, l->segments + l->n_segments);
+}
+
+nomas_status hip_fail(hipError_t e, const char* where) {
+  return fail(NOMAS_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool plan_matches_cache(const nomas_plan* p, const nomas_kvcache* c) {
+  if (!p->has_cache) return c == nullptr;
+  if (!c || c->id != p->cache_id) return false;
+  if ((int32_t)c->segs.size() != p->cache_nseg) return false;
+  const uint64_t last = c->serials.empty() ? 0 : c->serials.back();
+  return last == p->cache_last_serial;
+}
+
+nomas_status check_stride(int64_t stride, int32_t heads, const char* name) {
+  if (stride < (int64_t)heads * NOMAS_HEAD_DIM)
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " stride < heads * 128");
+  if (stride % 8 != 0) return fail(NOMAS_ERR_ALIGNMENT, std::string(name) + " stride not a multiple of 8");
+  return NOMAS_OK;
+}
+
+nomas_status check_dev_ptr(const void* p, bool needed, const char* name) {
+  if (!needed) return NOMAS_OK;
+  if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(NOMAS_ERR_ALIGNMENT, std::string(name) + " not 16-byte aligned");
+  return NOMAS_OK;
+}
+
+nomas_status check_device(const nomas_plan* p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan was built on another device");
+  return NOMAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nomas_status_string(nomas_status s) {
+  switch (s) {
+    case NOMAS_OK: return "ok";
+    case NOMAS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NOMAS_ERR_LAYOUT: return "malformed layout";
+    case NOMAS_ERR_UNSUPPORTED: return "unsupported";
+    case NOMAS_ERR_CAPACITY: return "cache capacity exceeded";
+    case NOMAS_ERR_STALE_PLAN: return "stale plan (cache changed)";
+    case NOMAS_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case NOMAS_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* nomas_last_error(void) { return t_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+// plans
+// ---------------------------------------------------------------------------
+
+nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
+                             const nomas_kvcache* cache, const nomas_plan_opts* opts,
+                             nomas_plan** out) {
+  if (!out) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!opts) return fail(NOMAS_ERR_INVALID_ARGUMENT, "opts is NULL");
+  nomas_status s;
+  if ((s = check_layout_ptr(q, "query")) != NOMAS_OK) return s;
+  if ((s = check_layout_ptr(kv_new, "kv_new")) != NOMAS_OK) return s;
+  if (cache && cache->heads != opts->num_heads)
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache heads differ from opts.num_heads");
+
+  nomas_plan* p = new (std::nothrow) nomas_plan();
+  if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out of host memory");
+  std::string err;
+  std::vector<nomas_segment> cached;
+  if (cache) cached = cache->segs;
+  try {
+    s = nomas::build_host_plan(to_vec(q), cached, to_vec(kv_new), *opts, &p->host, &err);
+  } catch (const std::bad_alloc&) {
+    s = NOMAS_ERR_INVALID_ARGUMENT;
+    err = "out of host memory while building the plan";
+  }
+  if (s != NOMAS_OK) {
+    delete p;
+    return fail(s, err);
+  }
+  if (cache) {
+    p->has_cache = true;
+    p->cache_id = cache->id;
+    p->cache_nseg = (int32_t)cache->segs.size();
+    p->cache_last_serial = cache->serials.empty() ? 0 : cache->serials.back();
+  }
+  if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
+    const nomas::HostPlan& h = p->host;
+    auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
+    const size_t b_q = al(h.qdesc.size() * sizeof(nomas::QDesc));
+    const size_t b_k = al(h.kdesc.size() * sizeof(nomas::KDesc));
+    const size_t b_rp = al(h.csr_ptr.size() * 4), b_ri = al(h.csr_idx.size() * 4 + 4);
+    const size_t b_cp = al(h.csc_ptr.size() * 4), b_ci = al(h.csc_idx.size() * 4 + 4);
+    const size_t total = b_q + b_k + b_rp + b_ri + b_cp + b_ci;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e == hipSuccess) e = hipMalloc(&p->dmem, total);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "plan upload");
+    }
+    char* base = static_cast<char*>(p->dmem);
+    struct Part { const void* src; size_t bytes; size_t room; };
+    const Part parts[] = {{h.qdesc.data(), h.qdesc.size() * sizeof(nomas::QDesc), b_q},
+                          {h.kdesc.data(), h.kdesc.size() * sizeof(nomas::KDesc), b_k},
+                          {h.csr_ptr.data(), h.csr_ptr.size() * 4, b_rp},
+                          {h.csr_idx.data(), h.csr_idx.size() * 4, b_ri},
+                          {h.csc_ptr.data(), h.csc_ptr.size() * 4, b_cp},
+                          {h.csc_idx.data(), h.csc_idx.size() * 4, b_ci}};
+    std::vector<char> staging(total, 0);
+    size_t off = 0;
+    for (const Part& part : parts) {
+      if (part.bytes) std::memcpy(staging.data() + off, part.src, part.bytes);
+      off += part.room;
+    }
+    e = hipMemcpy(p->dmem, staging.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p->dmem);
+      delete p;
+      return hip_fail(e, "plan upload");
+    }
+    p->d_qdesc = reinterpret_cast<const nomas::QDescDev*>(base);
+    p->d_kdesc = reinterpret_cast<const nomas::KDescDev*>(base + b_q);
+    p->d_csr_ptr = reinterpret_cast<const int32_t*>(base + b_q + b_k);
+    p->d_csr_idx = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp);
+    p->d_csc_ptr = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp + b_ri);
+    p->d_csc_idx = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp + b_ri + b_cp);
+    p->on_device = true;
+  }
+  *out = p;
+  return ok();
+}
+
+nomas_status nomas_plan_get_info(const nomas_plan* p, nomas_plan_info* info) {
+  if (!p || !info) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  const nomas::HostPlan& h = p->host;
+  info->n_queries = h.nq;
+  info->n_keys = h.nk;
+  info->n_cached_keys = h.n_cached;
+  info->n_q_tiles = h.nqt;
+  info->n_k_tiles = h.nkt;
+  info->n_empty_tiles = h.n_empty;
+  info->n_full_tiles = h.n_full;
+  info->n_partial_tiles = h.n_partial;
+  info->unmasked_pairs = h.unmasked_pairs;
+  info->executed_pairs = h.executed_pairs;
+  info->effective_flop = 4.0 * h.head_dim * h.heads * (double)h.unmasked_pairs;
+  info->block_q = h.bq;
+  info->block_k = h.bk;
+  info->num_heads = h.heads;
+  info->text_query_mode = h.mode;
+  return ok();
+}
+
+nomas_status nomas_plan_export_classes(const nomas_plan* p, uint8_t* buf, size_t n) {
+  if (!p || !buf) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (n < p->host.classes.size()) return fail(NOMAS_ERR_INVALID_ARGUMENT, "buffer too small");
+  std::memcpy(buf, p->host.classes.data(), p->host.classes.size());
+  return ok();
+}
+
+nomas_status nomas_plan_destroy(nomas_plan* p) {
+  if (!p) return ok();
+  if (p->dmem) (void)hipFree(p->dmem);
+  delete p;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+
+nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* p, size_t* bytes) {
+  if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  *bytes = 0;
+  return ok();
+}
+
+nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, const void* q,
+                            int64_t q_stride, const void* k_new, const void* v_new,
+                            int64_t kv_stride, void* o, int64_t o_stride, float* lse,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!p->on_device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "host-only plan cannot run");
+  if (!plan_matches_cache(p, cache))
+    return fail(p->has_cache && cache ? NOMAS_ERR_STALE_PLAN : NOMAS_ERR_INVALID_ARGUMENT,
+                p->has_cache && cache ? "cache changed since the plan was built"
+                                      : "cache argument does not match the plan");
+  const nomas::HostPlan& h = p->host;
+  const bool has_new = h.nk > h.n_cached;
+  nomas_status s;
+  if ((s = check_dev_ptr(q, h.nq > 0, "q")) || (s = check_dev_ptr(o, h.nq > 0, "o")) ||
+      (s = check_dev_ptr(k_new, has_new, "k_new")) || (s = check_dev_ptr(v_new, has_new, "v_new")))
+    return s;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NOMAS_ERR_ALIGNMENT, "lse misaligned");
+  if ((s = check_stride(q_stride, h.heads, "q")) || (s = check_stride(o_stride, h.heads, "o")))
+    return s;
+  if (has_new && (s = check_stride(kv_stride, h.heads, "kv"))) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if ((s = check_device(p))) return s;
+
+  nomas::FwdParams fp{};
+  fp.q = static_cast<const uint16_t*>(q);
+  fp.k_cache = cache ? static_cast<const uint16_t*>(cache->k) : nullptr;
+  fp.v_cache = cache ? static_cast<const uint16_t*>(cache->v) : nullptr;
+  fp.k_new = static_cast<const uint16_t*>(k_new);
+  fp.v_new = static_cast<const uint16_t*>(v_new);
+  fp.o = static_cast<uint16_t*>(o);
+  fp.lse = lse;
+  fp.qdesc = p->d_qdesc;
+  fp.kdesc = p->d_kdesc;
+  fp.csr_ptr = p->d_csr_ptr;
+  fp.csr_idx = p->d_csr_idx;
+  fp.q_stride = q_stride;
+  fp.kv_stride = kv_stride;
+  fp.o_stride = o_stride;
+  fp.cache_cap = cache ? cache->capacity : 0;
+  fp.nq = (int32_t)h.nq;
+  fp.nk = (int32_t)h.nk;
+  fp.n_cached = (int32_t)h.n_cached;
+  fp.heads = h.heads;
+  fp.nqt = (int32_t)h.nqt;
+  fp.nkt = (int32_t)h.nkt;
+  fp.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = nomas::launch_attn_fwd(fp, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* p, size_t* bytes) {
+  if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  *bytes = (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
+  return ok();
+}
+
+nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, const void* v,
+                            const void* o, const void* d_o, const float* lse, int64_t q_stride,
+                            int64_t kv_stride, void* dq, void* dk, void* dv, float scale,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!p->on_device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "host-only plan cannot run");
+  if (p->has_cache) return fail(NOMAS_ERR_INVALID_ARGUMENT, "backward needs a plan without a cache");
+  const nomas::HostPlan& h = p->host;
+  const bool hq = h.nq > 0, hk = h.nk > 0;
+  nomas_status s;
+  if ((s = check_dev_ptr(q, hq, "q")) || (s = check_dev_ptr(o, hq, "o")) ||
+      (s = check_dev_ptr(d_o, hq, "d_o")) || (s = check_dev_ptr(dq, hq, "dq")) ||
+      (s = check_dev_ptr(k, hk, "k")) || (s = check_dev_ptr(v, hk, "v")) ||
+      (s = check_dev_ptr(dk, hk, "dk")) || (s = check_dev_ptr(dv, hk, "dv")) ||
+      (s = check_dev_ptr(lse, hq, "lse")))
+    return s;
+  if ((s = check_stride(q_stride, h.heads, "q")) || (s = check_stride(kv_stride, h.heads, "kv")))
+    return s;
+  size_t need = 0;
+  nomas_attn_bwd_workspace_size(p, &need);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "workspace missing or too small");
+  if ((s = check_dev_ptr(workspace, need > 0, "workspace"))) return s;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if ((s = check_device(p))) return s;
+
+  nomas::BwdParams bp{};
+  bp.q = static_cast<const uint16_t*>(q);
+  bp.k = static_cast<const uint16_t*>(k);
+  bp.v = static_cast<const uint16_t*>(v);
+  bp.o = static_cast<const uint16_t*>(o);
+  bp.d_o = static_cast<const uint16_t*>(d_o);
+  bp.lse = lse;
+  bp.dq = static_cast<uint16_t*>(dq);
+  bp.dk = static_cast<uint16_t*>(dk);
+  bp.dv = static_cast<uint16_t*>(dv);
+  bp.delta = static_cast<float*>(workspace);
+  bp.qdesc = p->d_qdesc;
+  bp.kdesc = p->d_kdesc;
+  bp.csr_ptr = p->d_csr_ptr;
+  bp.csr_idx = p->d_csr_idx;
+  bp.csc_ptr = p->d_csc_ptr;
+  bp.csc_idx = p->d_csc_idx;
+  bp.q_stride = q_stride;
+  bp.kv_stride = kv_stride;
+  bp.nq = (int32_t)h.nq;
+  bp.nk = (int32_t)h.nk;
+  bp.heads = h.heads;
+  bp.nqt = (int32_t)h.nqt;
+  bp.nkt = (int32_t)h.nkt;
+  bp.scale = scale;
+  bp.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = nomas::launch_attn_bwd(bp, static_cast<hipStream_t>(hip_stream));
+  if (e == hipErrorNotSupported) return fail(NOMAS_ERR_UNSUPPORTED, "backward kernels not built");
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// KV cache
+// ---------------------------------------------------------------------------
+
+nomas_status nomas_kvcache_create(int32_t heads, int32_t head_dim, int64_t capacity, void* k_buf,
+                                  void* v_buf, nomas_kvcache** out) {
+  if (!out) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (heads < 1) return fail(NOMAS_ERR_INVALID_ARGUMENT, "heads must be >= 1");
+  if (head_dim != NOMAS_HEAD_DIM) return fail(NOMAS_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (capacity < 0 || capacity > (int64_t(1) << 30)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "capacity out of range");
+  nomas_status s;
+  if ((s = check_dev_ptr(k_buf, capacity > 0, "k_buf")) || (s = check_dev_ptr(v_buf, capacity > 0, "v_buf")))
+    return s;
+  nomas_kvcache* c = new (std::nothrow) nomas_kvcache();
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out of host memory");
+  c->heads = heads;
+  c->head_dim = head_dim;
+  c->capacity = capacity;
+  c->k = k_buf;
+  c->v = v_buf;
+  c->id = next_cache_id();
+  *out = c;
+  return ok();
+}
+
+nomas_status nomas_kvcache_append(nomas_kvcache* c, const nomas_segment* seg, const void* k_new,
+                                  const void* v_new, int64_t kv_stride, void* hip_stream) {
+  if (!c || !seg) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  std::string e = nomas::check_segment(*seg);
+  if (!e.empty()) return fail(NOMAS_ERR_LAYOUT, e);
+  for (const auto& s : c->segs)
+    if (s.video == seg->video && s.index == seg->index)
+      return fail(NOMAS_ERR_LAYOUT, "segment already in the cache");
+  const int64_t n = nomas::segment_tokens(*seg);
+  if (c->len + n > c->capacity) return fail(NOMAS_ERR_CAPACITY, "append would exceed the cache capacity");
+  nomas_status s;
+  if ((s = check_dev_ptr(k_new, true, "k_new")) || (s = check_dev_ptr(v_new, true, "v_new"))) return s;
+  if ((s = check_stride(kv_stride, c->heads, "kv"))) return s;
+  nomas::AppendParams ap{};
+  ap.k_src = static_cast<const uint16_t*>(k_new);
+  ap.v_src = static_cast<const uint16_t*>(v_new);
+  ap.k_dst = static_cast<uint16_t*>(c->k);
+  ap.v_dst = static_cast<uint16_t*>(c->v);
+  ap.src_stride = kv_stride;
+  ap.cap = c->capacity;
+  ap.dst_offset = c->len;
+  ap.tokens = (int32_t)n;
+  ap.heads = c->heads;
+  hipError_t he = nomas::launch_kvcache_append(ap, static_cast<hipStream_t>(hip_stream));
+  if (he != hipSuccess) return hip_fail(he, "kvcache_append launch");
+  c->segs.push_back(*seg);
+  c->serials.push_back(c->next_serial++);
+  c->len += n;
+  return ok();
+}
+
+nomas_status nomas_kvcache_truncate(nomas_kvcache* c, int32_t n_segments) {
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (n_segments < 0 || n_segments > (int32_t)c->segs.size())
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "n_segments out of range");
+  c->segs.resize((size_t)n_segments);
+  c->serials.resize((size_t)n_segments);
+  int64_t len = 0;
+  for (const auto& s : c->segs) len += nomas::segment_tokens(s);
+  c->len = len;
+  return ok();
+}
+
+nomas_status nomas_kvcache_reset(nomas_kvcache* c) { return nomas_kvcache_truncate(c, 0); }
+
+nomas_status nomas_kvcache_len(const nomas_kvcache* c, int64_t* n_tokens, int32_t* n_segments) {
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (n_tokens) *n_tokens = c->len;
+  if (n_segments) *n_segments = (int32_t)c->segs.size();
+  return ok();
+}
+
+nomas_status nomas_kvcache_destroy(nomas_kvcache* c) {
+  delete c;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace nomas {
+
+struct QDescDev {
+  int32_t seg, lo;
+  uint32_t amask;
+  int32_t pad_;
+};
+struct KDescDev {
+  int32_t seg;
+  uint32_t bits;
+};
+
+struct FwdParams {
+  const uint16_t* q;       // [nq][H][128] bf16, stride q_stride
+  const uint16_t* k_cache; // [H][cap][128] bf16 (or null)
+  const uint16_t* v_cache;
+  const uint16_t* k_new;   // [n_new][H][128] bf16, stride kv_stride
+  const uint16_t* v_new;
+  uint16_t* o;             // [nq][H][128] bf16, stride o_stride
+  float* lse;              // [H][nq] or null
+  const QDescDev* qdesc;   // nqt*128 entries
+  const KDescDev* kdesc;   // nkt*64 entries
+  const int32_t* csr_ptr;  // nqt+1
+  const int32_t* csr_idx;  // (k_tile << 1) | needs_mask
+  int64_t q_stride, kv_stride, o_stride, cache_cap;
+  int32_t nq, nk, n_cached, heads, nqt, nkt;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
+
+struct AppendParams {
+  const uint16_t* k_src;   // [T][H][128], stride src_stride
+  const uint16_t* v_src;
+  uint16_t* k_dst;         // [H][cap][128]
+  uint16_t* v_dst;
+  int64_t src_stride, cap, dst_offset;
+  int32_t tokens, heads;
+};
+
+hipError_t launch_kvcache_append(const AppendParams& p, hipStream_t stream);
+
+struct BwdParams {
+  const uint16_t *q, *k, *v, *o, *d_o;
+  const float* lse;        // [H][nq]
+  uint16_t *dq, *dk, *dv;
+  float* delta;            // workspace [H][nqt*128]
+  const QDescDev* qdesc;
+  const KDescDev* kdesc;
+  const int32_t *csr_ptr, *csr_idx, *csc_ptr, *csc_idx;
+  int64_t q_stride, kv_stride;
+  int32_t nq, nk, heads, nqt, nkt;
+  float scale, scale_log2;
+};
+
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace nomas

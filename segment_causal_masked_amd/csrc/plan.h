@@ -1,0 +1,72 @@
+// Host-side plan core: layout validation, per-token descriptors, tile classes,
+// CSR/CSC lists of non-empty tiles and the unmasked-pair count A.
+// Plain C++17, no HIP: it builds and runs on any host.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "nomas_attn.h"
+
+namespace nomas {
+
+// Per-token descriptors the kernels read (layout shared with the device code).
+//   query: seg   internal ordinal of the query's segment, -1 for padding
+//          lo    ordinal of the first segment of the query's video
+//          amask bit k set = the query sees tail a_k of its own segment
+//   key:   seg   ordinal of the key's segment, -1 for padding
+//          bits  (1 << k) for a token of tail a_k, 0 for video / head tokens
+// visible(q, k) = lo_q <= seg_k <= seg_q
+//                 && (bits_k == 0 || (seg_k == seg_q && (amask_q & bits_k)))
+// Ordinals number the distinct (video, index) pairs in lexicographic order, so
+// "same video and index_k <= index_q" is the ordinal range [lo_q, seg_q].
+struct QDesc {
+  int32_t seg, lo;
+  uint32_t amask;
+  int32_t pad_;
+};
+struct KDesc {
+  int32_t seg;
+  uint32_t bits;
+};
+
+inline bool visible(const QDesc& q, const KDesc& k) {
+  return k.seg >= q.lo && k.seg <= q.seg &&
+         (k.bits == 0u || (k.seg == q.seg && (q.amask & k.bits) != 0u));
+}
+
+// CSR/CSC entry: (tile << 1) | needs_mask, needs_mask = PARTIAL class or a
+// ragged last key tile (columns past the end must be masked).
+struct HostPlan {
+  int32_t heads = 0, head_dim = 0, bq = 0, bk = 0, mode = 0;
+  int64_t nq = 0, nk = 0, n_cached = 0;
+  int64_t nqt = 0, nkt = 0;
+  std::vector<QDesc> qdesc;   // nqt * bq entries (tail padded with seg = -1)
+  std::vector<KDesc> kdesc;   // nkt * bk entries (tail padded with seg = -1)
+  std::vector<uint8_t> classes;  // nqt * nkt, NOMAS_TILE_*
+  std::vector<int32_t> csr_ptr, csr_idx;  // per q-tile
+  std::vector<int32_t> csc_ptr, csc_idx;  // per k-tile
+  int64_t n_empty = 0, n_full = 0, n_partial = 0;
+  int64_t unmasked_pairs = 0, executed_pairs = 0;
+};
+
+// Identity of a cache's committed segments (used for stale-plan checks).
+struct CacheState {
+  int32_t n_segments = 0;
+  uint64_t last_serial = 0;
+};
+
+// Validate one record; returns "" or a description of the problem.
+std::string check_segment(const nomas_segment& s);
+int64_t segment_tokens(const nomas_segment& s);
+
+// Build the host plan.  keys = cached ++ kv_new.  Returns NOMAS_OK or an
+// error status with *err filled.
+nomas_status build_host_plan(const std::vector<nomas_segment>& q,
+                             const std::vector<nomas_segment>& cached,
+                             const std::vector<nomas_segment>& kv_new,
+                             const nomas_plan_opts& opts, HostPlan* out,
+                             std::string* err);
+
+}  // namespace nomas

@@ -1,0 +1,76 @@
+"""Helpers shared by the GPU parity tests (inputs on the device, tolerances)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import segment_causal_masked_amd as nm
+
+SCALE = 128 ** -0.5
+
+# Gate from the method's brief: max-abs 1e-2 and mean-abs 1e-3 on unit-scale
+# outputs (inputs ~ N(0,1)); LSE is fp32 end to end, so a tighter bound holds.
+O_MAX_ABS, O_MEAN_ABS, LSE_ABS = 1e-2, 1e-3, 2e-3
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nm.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype=torch.bfloat16):
+    """numpy fp32 (bf16-representable) -> device tensor (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype)
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+def check_o(o_gpu, o_ref, what=""):
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    say(f"  {what}: O max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, (what, mx, mean)
+    assert np.isfinite(o_gpu).all()
+
+
+def check_lse(lse_gpu, lse_ref, what=""):
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), what
+    assert np.all(lse_gpu[~fin] == -np.inf)
+    if fin.any():
+        d = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max())
+        say(f"  {what}: LSE max-abs {d:.3e}")
+        assert d <= LSE_ABS, (what, d)
+
+
+def new_cache(heads, capacity):
+    kb = torch.zeros((heads, capacity, 128), dtype=torch.bfloat16, device="cuda")
+    vb = torch.zeros_like(kb)
+    return nm.nomas_kvcache_create(heads, capacity, kb, vb)
+
+
+def fill_cache(cache, segments, k_tok, v_tok):
+    """Append segments one by one from token-major [T,H,D] device tensors."""
+    off = 0
+    for s in segments:
+        n = s.n_tokens
+        nm.nomas_kvcache_append(cache, s, k_tok[off:off + n], v_tok[off:off + n])
+        off += n
+    return off
+
+
+def run_fwd(plan, cache, q, k_new, v_new, heads, lse=True):
+    o = torch.empty((q.shape[0], heads, 128), dtype=torch.bfloat16, device="cuda")
+    l = torch.empty((heads, q.shape[0]), dtype=torch.float32, device="cuda") if lse else None
+    nm.nomas_attn_fwd(plan, cache, q, k_new, v_new, o, l, SCALE)
+    torch.cuda.synchronize()
+    return o, l

@@ -1,0 +1,173 @@
+"""Host side of the C ABI, on the CPU: the library loads, exports every
+function the header declares, and its plan (descriptors, tile classes, A)
+agrees bit for bit with the oracle.  No kernel is launched here."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+import oracle
+import segment_causal_masked_amd as nm
+from segment_causal_masked_amd import _lib
+from segment_causal_masked_amd import workloads as wl
+from golden_io import load_mask_fixture
+from test_oracle_mask import random_tiny_layout
+
+
+def test_library_exports_every_header_function():
+    lib = nm.load()
+    names = _lib.header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def host_plan(q, kv, heads=1, mode="R", bq=0, bk=0):
+    return nm.nomas_attn_plan(q, kv, heads=heads, mode=mode, host_only=True, block_q=bq, block_k=bk)
+
+
+@pytest.mark.parametrize("name", ["config1_mask.txt", "pack2_mask.txt"])
+def test_plan_matches_hand_built_fixtures(name):
+    segs, mask, A, (bq, bk), tmap = load_mask_fixture(name)
+    for mode in ("R", "K", "H"):
+        p = host_plan(segs, segs, mode=mode, bq=bq, bk=bk)
+        assert p.info().unmasked_pairs == A[mode]
+        if mode == "R":
+            np.testing.assert_array_equal(nm.nomas_plan_export_classes(p), tmap)
+
+
+def test_plan_classes_random_layouts_and_tiles():
+    g = np.random.default_rng(2024)
+    for trial in range(150):
+        segs = random_tiny_layout(g, n_videos=int(g.integers(1, 4)))
+        mode = "RKH"[trial % 3]
+        bq, bk = int(g.integers(1, 9)), int(g.integers(1, 9))
+        # queries: a random sub-list of the segments; keys: all of them
+        nq = int(g.integers(1, len(segs) + 1))
+        qsegs = [segs[i] for i in sorted(g.choice(len(segs), nq, replace=False))]
+        p = host_plan(qsegs, segs, mode=mode, bq=bq, bk=bk)
+        tq, tk = oracle.expand(qsegs), oracle.expand(segs)
+        np.testing.assert_array_equal(nm.nomas_plan_export_classes(p),
+                                      oracle.tile_classes(tq, tk, bq, bk, mode))
+        assert p.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk, mode)
+
+
+@pytest.mark.parametrize("cfg,mode", [(1, "R"), (2, "R"), (2, "K"), (2, "H"), (3, "R"), (3, "H")])
+def test_plan_classes_configs(cfg, mode):
+    w = wl.CONFIGS[cfg]()
+    keys = w.cached + w.new
+    p = host_plan(w.q_layout, keys, heads=w.heads, mode=mode)
+    info = p.info()
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    cls = nm.nomas_plan_export_classes(p)
+    np.testing.assert_array_equal(cls, oracle.tile_classes(tq, tk, 128, 64, mode))
+    assert info.unmasked_pairs == oracle.unmasked_pairs(tq, tk, mode)
+    assert info.n_full_tiles == int((cls == 1).sum())
+    assert info.effective_flop == 4.0 * 128 * w.heads * info.unmasked_pairs
+
+
+@pytest.mark.slow
+def test_plan_classes_config4_full():
+    w = wl.config4()
+    keys = w.cached + w.new
+    p = host_plan(w.q_layout, keys, heads=16)
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    np.testing.assert_array_equal(nm.nomas_plan_export_classes(p),
+                                  oracle.tile_classes(tq, tk, 128, 64))
+    assert p.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk)
+
+
+def test_plan_classes_config5_sampled_tiles():
+    w = wl.config5()
+    p = host_plan(w.q_layout, w.new, heads=16)
+    t = oracle.expand(w.q_layout)
+    cls = nm.nomas_plan_export_classes(p)
+    assert cls.shape == (1024, 2048)
+    rows = list(range(0, 1024, 67)) + [1023]
+    np.testing.assert_array_equal(cls[rows], oracle.tile_classes(t, t, 128, 64, q_tiles=rows))
+    # A by the hand-derived closed form (all videos, all segments)
+    from test_oracle_mask import closed_form_A
+    assert p.info().unmasked_pairs == closed_form_A(w.q_layout)
+    dens = p.info().unmasked_pairs / float(131072) ** 2
+    assert 0.05 < dens < 0.25
+
+
+# ----------------------------------------------------------------------------
+# error paths (all caught on the host before any device work)
+# ----------------------------------------------------------------------------
+
+def seg(**kw):
+    base = dict(video=0, index=0, n_frames=2, tokens_per_frame=4, n_head=2,
+                actions=[(2, 0, 1)], n_pad=0)
+    base.update(kw)
+    return wl.Segment(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    seg(actions=[(2, 1, 1)]),            # lo == hi
+    seg(actions=[(2, 0, 3)]),            # hi > n_frames
+    seg(actions=[(0, 0, 1)]),            # tail without tokens
+    seg(actions=[(1, 0, 1)] * 33),       # more than 32 actions
+    seg(n_frames=0, tokens_per_frame=0, n_head=0, actions=[]),  # empty segment
+    seg(video=-1),
+])
+def test_layout_errors(bad):
+    with pytest.raises(nm.NomasError) as e:
+        host_plan([bad], [bad])
+    assert e.value.status == _lib.ERR_LAYOUT
+
+
+def test_duplicate_and_mismatched_segments():
+    a, b = seg(), seg(n_head=3)
+    with pytest.raises(nm.NomasError) as e:
+        host_plan([a], [a, a])
+    assert e.value.status == _lib.ERR_LAYOUT
+    with pytest.raises(nm.NomasError) as e:
+        host_plan([a], [b])
+    assert e.value.status == _lib.ERR_LAYOUT
+
+
+def test_unsupported_options():
+    a = seg()
+    lib = nm.load()
+    lay = _lib._Layout([a])
+    out = C.c_void_p()
+    for hd, bq, bk, want in ((64, 0, 0, _lib.ERR_UNSUPPORTED), (128, 64, 64, _lib.ERR_UNSUPPORTED),
+                             (128, 0, 0, _lib.OK)):
+        opts = _lib.nomas_plan_opts(1, hd, bq, bk, 0, 0, 0, 0)
+        st = lib.nomas_attn_plan(C.byref(lay.c), C.byref(lay.c), None, C.byref(opts), C.byref(out))
+        if want == _lib.OK:
+            # a device plan needs a device; without one the upload fails with a HIP error
+            assert st in (_lib.OK, _lib.ERR_HIP)
+            if st == _lib.OK:
+                lib.nomas_plan_destroy(out)
+        else:
+            assert st == want, nm.nomas_last_error()
+    opts = _lib.nomas_plan_opts(1, 128, 0, 0, 7, 1, 0, 0)
+    assert lib.nomas_attn_plan(C.byref(lay.c), C.byref(lay.c), None, C.byref(opts),
+                               C.byref(out)) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.nomas_attn_plan(None, C.byref(lay.c), None, C.byref(opts),
+                               C.byref(out)) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_host_only_plan_cannot_run_and_cache_checks():
+    a = seg()
+    p = host_plan([a], [a])
+    lib = nm.load()
+    st = lib.nomas_attn_fwd(p.handle, None, C.c_void_p(256), 128, C.c_void_p(256), C.c_void_p(256),
+                            128, C.c_void_p(256), 128, None, 0.1, None, 0, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT
+    assert "host-only" in nm.nomas_last_error()
+    # cache bookkeeping on fake, aligned addresses (never dereferenced here)
+    c = C.c_void_p()
+    assert lib.nomas_kvcache_create(1, 128, 10, C.c_void_p(256), C.c_void_p(512), C.byref(c)) == 0
+    assert lib.nomas_kvcache_create(1, 128, 10, C.c_void_p(258), C.c_void_p(512),
+                                    C.byref(C.c_void_p())) == _lib.ERR_ALIGNMENT
+    big = _lib.to_c_segment(seg(n_frames=3, tokens_per_frame=4, actions=[]))  # 14 tokens > 10
+    st = lib.nomas_kvcache_append(c, C.byref(big), C.c_void_p(256), C.c_void_p(256), 128, None)
+    assert st == _lib.ERR_CAPACITY
+    n, s = C.c_int64(-1), C.c_int32(-1)
+    assert lib.nomas_kvcache_len(c, C.byref(n), C.byref(s)) == 0 and (n.value, s.value) == (0, 0)
+    assert lib.nomas_kvcache_truncate(c, 1) == _lib.ERR_INVALID_ARGUMENT
+    lib.nomas_kvcache_destroy(c)
+    assert nm.nomas_status_string(_lib.ERR_STALE_PLAN).startswith("stale")

@@ -1,0 +1,249 @@
+"""GPU parity of the forward kernel and the cache append against the fp64
+oracle, through the C ABI, plus the method's invariants checked bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import segment_causal_masked_amd as nm
+from segment_causal_masked_amd import workloads as wl
+from gpu_util import (SCALE, check_lse, check_o, dev, fill_cache, host, need_gpu, new_cache,
+                      run_fwd, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def dense_case(w, mode="R", nfe=0):
+    """Plan + inputs for a workload whose keys are all passed with the call."""
+    keys = w.cached + w.new
+    q = w.q(nfe)
+    if w.cached:
+        kc, vc = w.cache_kv()
+        k = np.concatenate([kc, w.k_new(nfe)])
+        v = np.concatenate([vc, w.v_new(nfe)])
+    else:
+        k, v = w.k_new(nfe), w.v_new(nfe)
+    plan = nm.nomas_attn_plan(w.q_layout, keys, heads=w.heads, mode=mode)
+    return plan, q, k, v, keys
+
+
+def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None):
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    return oracle.forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads)
+
+
+def test_config1_tiny_fp32_inputs():
+    need_gpu()
+    w = wl.config1()
+    say("config1 tiny: 96 tokens, 1 head, fp32 inputs rounded to bf16 for the kernel")
+    plan, q, k, v, keys = dense_case(w)
+    o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 1)
+    o_ref, l_ref = oracle_fwd(w, q, k, v, keys)            # oracle on the fp32 inputs
+    check_o(host(o), o_ref, "vs fp32 inputs")
+    check_lse(host(l), l_ref, "vs fp32 inputs")
+    qb, kb, vb = (wl.round_to_bf16(x) for x in (q, k, v))
+    o_ref_b, l_ref_b = oracle_fwd(w, qb, kb, vb, keys)     # same bf16 values
+    check_o(host(o), o_ref_b, "vs bf16 inputs")
+    check_lse(host(l), l_ref_b, "vs bf16 inputs")
+
+
+@pytest.mark.parametrize("mode", ["R", "K", "H"])
+def test_config2_single_segment(mode):
+    need_gpu()
+    w = wl.config2()
+    say(f"config2 single 480p segment, 3280 tokens x 16 heads, mode {mode}")
+    plan, q, k, v, keys = dense_case(w, mode)
+    o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
+    heads = None if mode == "R" else [0, 7, 15]
+    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, mode=mode, heads=heads)
+    hsel = slice(None) if heads is None else heads
+    check_o(host(o)[:, hsel], o_ref, f"config2 {mode}")
+    check_lse(host(l)[hsel], l_ref, f"config2 {mode}")
+
+
+def test_config2_sorted_windows_seed_set():
+    need_gpu()
+    w = wl.config2(seed_set=1)
+    plan, q, k, v, keys = dense_case(w)
+    o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
+    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, heads=[3, 12])
+    check_o(host(o)[:, [3, 12]], o_ref, "config2 sorted windows")
+    check_lse(host(l)[[3, 12]], l_ref, "config2 sorted windows")
+
+
+def build_cached(w, layer=0):
+    kc, vc = w.cache_kv(layer)
+    cap = w.n_cached + w.n_new
+    cache = new_cache(w.heads, cap)
+    kd, vd = dev(kc), dev(vc)
+    fill_cache(cache, w.cached, kd, vd)
+    torch.cuda.synchronize()
+    return cache, kc, vc
+
+
+def test_config3_cached_step_and_append_layout():
+    need_gpu()
+    w = wl.config3()
+    say("config3 480p cached step: 4 cached segments (13120 keys) + 3280 new, 16 heads")
+    cache, kc, vc = build_cached(w)
+    # the append wrote token-major rows into the head-major cache, bit for bit
+    kb = cache.k_buf[:, :w.n_cached].permute(1, 0, 2).contiguous()
+    vb = cache.v_buf[:, :w.n_cached].permute(1, 0, 2).contiguous()
+    assert torch.equal(kb, dev(kc)) and torch.equal(vb, dev(vc))
+    assert nm.nomas_kvcache_len(cache) == (w.n_cached, 4)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
+    q, kn, vn = w.q(), w.k_new(), w.v_new()
+    o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
+    keys = w.cached + w.new
+    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys)
+    check_o(host(o), o_ref, "config3")
+    check_lse(host(l), l_ref, "config3")
+
+
+def test_config3_cached_equals_full_sequence_bitwise():
+    """Cached decoding of the last segment == its rows of the full-sequence run."""
+    need_gpu()
+    w = wl.config3()
+    cache, kc, vc = build_cached(w)
+    q, kn, vn = w.q(), w.k_new(), w.v_new()
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
+    o_c, l_c = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
+    full = w.cached + w.new
+    g = np.random.default_rng(0)
+    q_full = np.concatenate([wl.round_to_bf16(g.standard_normal((w.n_cached, 16, 128), np.float32)), q])
+    k_full, v_full = np.concatenate([kc, kn]), np.concatenate([vc, vn])
+    plan_f = nm.nomas_attn_plan(full, full, heads=16)
+    o_f, l_f = run_fwd(plan_f, None, dev(q_full), dev(k_full), dev(v_full), 16)
+    d = (o_c.float() - o_f[w.n_cached:].float()).abs()
+    say(f"  cached vs full rows: bitwise equal {torch.equal(o_c, o_f[w.n_cached:])}, "
+        f"max-abs {float(d.max()):.3e}")
+    assert float(d.max()) <= 1e-2 and float(d.mean()) <= 1e-3
+    assert float((l_c - l_f[:, w.n_cached:]).abs().max()) <= 2e-3
+    # segment j is unchanged by the contents of segment j+1 (bitwise)
+    k2, v2 = k_full.copy(), v_full.copy()
+    k2[w.n_cached:] += 1.0
+    v2[w.n_cached:] -= 1.0
+    o_p, _ = run_fwd(plan_f, None, dev(q_full), dev(k2), dev(v2), 16)
+    assert torch.equal(o_p[:w.n_cached], o_f[:w.n_cached])
+    assert not torch.equal(o_p[w.n_cached:], o_f[w.n_cached:])
+
+
+def test_masked_kv_perturbation_is_invisible_bitwise():
+    need_gpu()
+    w = wl.config2()
+    plan, q, k, v, keys = dense_case(w)
+    o0, l0 = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
+    s = w.q_layout[0]
+    n_video = s.n_frames * s.tokens_per_frame
+    start = n_video + s.n_head                     # a_0's tokens
+    n0, lo, hi = s.actions[0]
+    k2, v2 = k.copy(), v.copy()
+    k2[start:start + n0] = 5.0
+    v2[start:start + n0] = -3.0
+    o1, _ = run_fwd(plan, None, dev(q), dev(k2), dev(v2), 16)
+    changed = (o1 != o0).any(dim=2).any(dim=1).cpu().numpy()
+    t = oracle.expand(w.q_layout)
+    m = oracle.visible_mask(t, t)
+    sees_a0 = m[:, start:start + n0].any(axis=1)
+    say(f"  rows seeing a_0: {int(sees_a0.sum())}, rows changed: {int(changed.sum())}")
+    assert not changed[~sees_a0].any()             # invisible everywhere else, bit for bit
+    assert changed[sees_a0].all()                  # and visible where it should be
+    frames = np.flatnonzero(sees_a0[:n_video]) // s.tokens_per_frame
+    assert frames.min() >= lo and frames.max() < hi
+
+
+def test_padding_rows_and_ragged_shapes():
+    need_gpu()
+    segs = [wl.Segment(0, 0, 3, 7, 5, [(3, 0, 2), (2, 2, 3)], n_pad=9),
+            wl.Segment(1, 0, 2, 50, 4, [(6, 1, 2)], n_pad=1),
+            wl.Segment(1, 1, 5, 33, 17, [(1, 0, 5), (4, 3, 4), (2, 1, 3)], n_pad=3)]
+    n = sum(s.n_tokens for s in segs)
+    say(f"ragged pack: {n} tokens, 3 heads, padding rows")
+    g = np.random.default_rng(1)
+    q, k, v = (wl.round_to_bf16(g.standard_normal((n, 3, 128), np.float32)) for _ in range(3))
+    plan = nm.nomas_attn_plan(segs, segs, heads=3)
+    o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 3)
+    t = oracle.expand(segs)
+    o_ref, l_ref = oracle.forward(q, k, v, t, t, SCALE)
+    check_o(host(o), o_ref, "ragged pack")
+    check_lse(host(l), l_ref, "ragged pack")
+    pad = t.kind == oracle.PAD
+    assert (host(o)[pad] == 0).all()
+
+
+def test_single_token_and_empty_query():
+    need_gpu()
+    s1 = [wl.Segment(0, 0, 1, 1, 0, [])]
+    q = dev(wl.randn((1, 2, 128), 5))
+    plan = nm.nomas_attn_plan(s1, s1, heads=2)
+    o, l = run_fwd(plan, None, q, q, q, 2)
+    assert torch.allclose(o.float(), q.float(), atol=0, rtol=2 ** -8)   # softmax over one key
+    # no queries: a no-op that still validates arguments
+    plan0 = nm.nomas_attn_plan([], s1, heads=2)
+    o0 = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    nm.nomas_attn_fwd(plan0, None, o0, q, q, o0, None, SCALE)
+    torch.cuda.synchronize()
+
+
+def test_stale_plan_after_append_and_truncate():
+    need_gpu()
+    w = wl.config3(n_cached=2)
+    cache, kc, vc = build_cached(w)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
+    q, kn, vn = dev(w.q()), dev(w.k_new()), dev(w.v_new())
+    o_a, _ = run_fwd(plan, cache, q, kn, vn, 16)
+    nm.nomas_kvcache_append(cache, w.new[0], kn, vn)
+    with pytest.raises(nm.NomasError) as e:
+        run_fwd(plan, cache, q, kn, vn, 16)
+    assert e.value.status == 5
+    nm.nomas_kvcache_truncate(cache, 2)          # back to the contents the plan saw
+    o_b, _ = run_fwd(plan, cache, q, kn, vn, 16)
+    assert torch.equal(o_a, o_b)
+    # capacity: nothing written, nothing recorded
+    small = new_cache(16, 100)
+    before = small.k_buf.clone()
+    with pytest.raises(nm.NomasError) as e:
+        nm.nomas_kvcache_append(small, w.new[0], kn, vn)
+    assert e.value.status == 4 and nm.nomas_kvcache_len(small) == (0, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, small.k_buf)
+
+
+def test_config4_long_session_sampled_rows():
+    """Full 720p session shape (16 cached segments, 122944 keys), 4 denoising
+    calls, then the append; outputs checked on sampled rows and heads."""
+    need_gpu()
+    w = wl.config4()
+    say("config4 720p: 16 cached x 7232 + 7232 new = 122944 keys, 4 calls")
+    cache, kc, vc = build_cached(w)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
+    keys = w.cached + w.new
+    g = np.random.default_rng(44)
+    rows = np.sort(np.concatenate([g.choice(w.n_q, 40, replace=False),
+                                   np.arange(w.n_q - 300, w.n_q, 37)]))
+    heads = [2, 9]
+    for nfe in range(4):
+        q, kn, vn = w.q(nfe), w.k_new(nfe), w.v_new(nfe)
+        o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
+        o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+                                  rows=rows, heads=heads)
+        check_o(host(o)[rows][:, heads], o_ref, f"config4 call {nfe}")
+        check_lse(host(l)[heads][:, rows], l_ref, f"config4 call {nfe}")
+    nm.nomas_kvcache_append(cache, w.new[0], dev(kn), dev(vn))   # K/V of the last call
+    torch.cuda.synchronize()
+    assert nm.nomas_kvcache_len(cache) == (w.n_cached + w.n_new, 17)
+    got = cache.k_buf[:, w.n_cached:].permute(1, 0, 2)
+    assert torch.equal(got, dev(kn))
+
+
+def test_config5_training_pack_forward_sampled():
+    need_gpu()
+    w = wl.config5()
+    say("config5 training pack: 131072 tokens, 4 videos, forward on sampled rows")
+    plan, q, k, v, keys = dense_case(w)
+    o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
+    g = np.random.default_rng(55)
+    rows = np.sort(g.choice(w.n_q, 48, replace=False))
+    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, rows=rows, heads=[0, 13])
+    check_o(host(o)[rows][:, [0, 13]], o_ref, "config5 fwd")
+    check_lse(host(l)[[0, 13]][:, rows], l_ref, "config5 fwd")
