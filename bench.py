@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark: effective TFLOP/s of the action-aware causal attention forward.
+
+Workload (default): the 480p segment-autoregressive step -- 4 cached segments
+(3120 video + 64 head + 3 x 32 tail tokens each) plus the new segment as
+queries, 16 heads x 128, bf16.  One timed *step* is one segment step of the
+denoising loop over L layers: for each of the 4 denoising calls, the forward
+of every layer (each layer reads its own cache, so no call finds its K/V warm
+in the last-level cache), then the append of the new segment's K/V to every
+layer's cache.  The host plan is built once per segment step and shared by all
+layers and calls; its time is reported separately.
+
+value = 4 * 128 * 16 * A * (4 calls * L layers) / step time, A = unmasked pairs.
+roofline = the forward kernel: the same effective FLOPs per launch / the
+launch's average duration (HIP events on the launch stream), against the bf16
+dense MFMA peak of MI355X.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_hash():
+    src = os.path.join(ROOT, "segment_causal_masked_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per forward launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_480p_cached_step_traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, heads=4):
+    """The fp64 oracle on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    keys = w.cached + w.new
+    kc, vc = w.cache_kv()
+    q = w.q()[:, :heads]
+    k = np.concatenate([kc, w.k_new()])[:, :heads]
+    v = np.concatenate([vc, w.v_new()])[:, :heads]
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, tq, tk, 128 ** -0.5)
+    dt = time.perf_counter() - t0
+    a = oracle.unmasked_pairs(tq, tk)
+    flop = 4.0 * 128 * heads * a
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: {heads} of 16 heads, all {w.n_q} queries x {w.n_keys} keys, "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention is sharded by heads across GPUs outside this library).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import segment_causal_masked_amd as nm
+    from segment_causal_masked_amd import workloads as wl
+
+    nm.load()
+    torch.cuda.set_device(0)
+    w = wl.config3()
+    H, D, L, NFE = w.heads, 128, args.layers, 4
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(torch.bfloat16)
+
+    kc, vc = w.cache_kv()
+    kc_d, vc_d = dev(kc), dev(vc)
+    caches = []
+    for layer in range(L):
+        kb = torch.empty((H, w.n_cached + w.n_new, D), dtype=torch.bfloat16, device="cuda")
+        vb = torch.empty_like(kb)
+        c = nm.nomas_kvcache_create(H, w.n_cached + w.n_new, kb, vb)
+        off = 0
+        for s in w.cached:
+            nm.nomas_kvcache_append(c, s, kc_d[off:off + s.n_tokens], vc_d[off:off + s.n_tokens])
+            off += s.n_tokens
+        caches.append(c)
+    del kc_d, vc_d
+    t0 = time.perf_counter()
+    plans = [nm.nomas_attn_plan(w.q_layout, w.new, c, heads=H) for c in caches]
+    plan_ms = (time.perf_counter() - t0) * 1e3 / L
+    info = plans[0].info()
+    A = info.unmasked_pairs
+    flop_call = 4.0 * D * H * A
+
+    qs = [dev(w.q(n)) for n in range(NFE)]
+    ks = [dev(w.k_new(n)) for n in range(NFE)]
+    vs = [dev(w.v_new(n)) for n in range(NFE)]
+    outs = [torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    lses = [torch.empty((H, w.n_q), dtype=torch.float32, device="cuda") for _ in range(L)]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    n_cached_segs = len(w.cached)
+
+    def step(fwd_events=None, app_events=None):
+        for n in range(NFE):
+            for layer in range(L):
+                if fwd_events is not None:
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                nm.nomas_attn_fwd(plans[layer], caches[layer], qs[n], ks[n], vs[n], outs[layer],
+                                  lses[layer], D ** -0.5)
+                if fwd_events is not None:
+                    e1.record(stream)
+                    fwd_events.append((e0, e1))
+        for layer in range(L):
+            if app_events is not None:
+                a0, a1 = ev(), ev()
+                a0.record(stream)
+            nm.nomas_kvcache_append(caches[layer], w.new[0], ks[NFE - 1], vs[NFE - 1])
+            if app_events is not None:
+                a1.record(stream)
+                app_events.append((a0, a1))
+        # roll the caches back to the segment step's starting contents (host
+        # bookkeeping only); the plans built for those contents stay valid
+        for c in caches:
+            nm.nomas_kvcache_truncate(c, n_cached_segs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: whole steps
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # timed region 2: the same steps with per-launch events
+    fwd_ev, app_ev = [], []
+    for _ in range(args.steps):
+        step(fwd_ev, app_ev)
+    torch.cuda.synchronize()
+    fwd_ms = np.array([a.elapsed_time(b) for a, b in fwd_ev])
+    app_ms = np.array([a.elapsed_time(b) for a, b in app_ev])
+
+    value = flop_call * NFE * L / (ms_step * 1e-3) / 1e12
+    fwd_avg = float(fwd_ms.mean())
+    achieved = flop_call / (fwd_avg * 1e-3) / 1e12
+    traffic = traffic_from_profiles(w.name)
+    app_bytes = 2 * 2 * w.n_new * H * D * 2  # K and V, read + write
+    line = {
+        "metric": "effective TFLOP/s of action-aware causal attn fwd; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "queries": w.n_q, "keys": w.n_keys, "heads": H,
+                   "head_dim": D, "cached_segments": n_cached_segs, "denoising_calls": NFE,
+                   "layers_per_step": L, "unmasked_pairs": A,
+                   "tiles": {"full": info.n_full_tiles, "partial": info.n_partial_tiles,
+                             "empty": info.n_empty_tiles}},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "fwd_ms_per_call": round(fwd_avg, 4),
+        "fwd_ms_min": round(float(fwd_ms.min()), 4),
+        "executed_over_effective": round(info.executed_pairs / A, 4),
+        "append_ms": round(float(app_ms.mean()), 4),
+        "append_gbs": round(app_bytes / (float(app_ms.mean()) * 1e-3) / 1e9, 1),
+        "plan_host_ms": round(plan_ms, 3),
+        "kernel_sha": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -286,4 +286,56 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   return NOMAS_OK;
 }
 
+void build_fwd_schedule(HostPlan* pp, int32_t groups) {
+  HostPlan& p = *pp;
+  const int64_t n_units = int64_t(p.heads) * p.nqt;
+  const int64_t row_total = p.csr_ptr.empty() ? 0 : p.csr_ptr.back();
+  const int64_t total = int64_t(p.heads) * row_total;
+  groups = std::max<int32_t>(1, groups);
+  p.fwd_groups = groups;
+  p.pieces.clear();
+  p.combine.clear();
+  p.n_slots = 0;
+  std::vector<std::vector<Piece>> per(static_cast<size_t>(groups));
+  auto bound = [&](int64_t g) { return (total * g) / groups; };
+  auto group_of = [&](int64_t it) {  // the range holding iteration `it`
+    int64_t g = (it * groups) / std::max<int64_t>(total, 1);
+    while (g + 1 < groups && bound(g + 1) <= it) ++g;
+    while (g > 0 && bound(g) > it) --g;
+    return std::min<int64_t>(g, groups - 1);
+  };
+  for (int64_t u = 0; u < n_units; ++u) {
+    const int64_t h = u / p.nqt, qt = u % p.nqt;
+    const int64_t n = p.csr_ptr[size_t(qt + 1)] - p.csr_ptr[size_t(qt)];
+    const int64_t start = h * row_total + p.csr_ptr[size_t(qt)];
+    if (n == 0) {  // nothing visible: still owes zeros / -inf to its rows
+      per[size_t(group_of(std::min(start, std::max<int64_t>(total - 1, 0))))].push_back(
+          Piece{int32_t(u), 0, 0, -1});
+      continue;
+    }
+    const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
+    const int32_t first_slot = p.n_slots;
+    for (int64_t g = g0; g <= g1; ++g) {
+      const int64_t a = std::max(bound(g), start), b = std::min(bound(g + 1), start + n);
+      if (a >= b) continue;
+      per[size_t(g)].push_back(Piece{int32_t(u), int32_t(a - start), int32_t(b - start), -1});
+    }
+    // count the pieces actually made (ranges of zero width were skipped)
+    int32_t made = 0;
+    for (int64_t g = g0; g <= g1; ++g)
+      if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u)) ++made;
+    if (made > 1) {
+      for (int64_t g = g0; g <= g1; ++g)
+        if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u))
+          per[size_t(g)].back().slot = p.n_slots++;
+      p.combine.push_back(CombineItem{int32_t(u), first_slot, made, 0});
+    }
+  }
+  p.wg_ptr.assign(size_t(groups) + 1, 0);
+  for (int32_t g = 0; g < groups; ++g) {
+    p.pieces.insert(p.pieces.end(), per[size_t(g)].begin(), per[size_t(g)].end());
+    p.wg_ptr[size_t(g) + 1] = int32_t(p.pieces.size());
+  }
+}
+
 }  // namespace nomas

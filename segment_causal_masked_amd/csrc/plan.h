@@ -36,6 +36,18 @@ inline bool visible(const QDesc& q, const KDesc& k) {
          (k.bits == 0u || (k.seg == q.seg && (q.amask & k.bits) != 0u));
 }
 
+// Forward work schedule.  The iterations of the forward are (unit, entry)
+// pairs, unit = head * n_q_tiles + q_tile, entry = position in the q-tile's
+// list of non-empty key tiles.  They are cut into `groups` contiguous,
+// equal ranges, one per persistent workgroup; a unit cut by a range boundary
+// becomes several pieces whose partial results are merged afterwards.
+struct Piece {
+  int32_t unit, e_begin, e_end, slot;  // slot = partial-result slot, -1 = final
+};
+struct CombineItem {
+  int32_t unit, first_slot, n_pieces, pad_;
+};
+
 // CSR/CSC entry: (tile << 1) | needs_mask, needs_mask = PARTIAL class or a
 // ragged last key tile (columns past the end must be masked).
 struct HostPlan {
@@ -49,7 +61,16 @@ struct HostPlan {
   std::vector<int32_t> csc_ptr, csc_idx;  // per k-tile
   int64_t n_empty = 0, n_full = 0, n_partial = 0;
   int64_t unmasked_pairs = 0, executed_pairs = 0;
+  // forward schedule (build_fwd_schedule)
+  int32_t fwd_groups = 0;
+  std::vector<int32_t> wg_ptr;        // fwd_groups + 1
+  std::vector<Piece> pieces;
+  std::vector<CombineItem> combine;
+  int32_t n_slots = 0;
 };
+
+// Cut the forward iterations into `groups` equal contiguous ranges.
+void build_fwd_schedule(HostPlan* p, int32_t groups);
 
 // Identity of a cache's committed segments (used for stale-plan checks).
 struct CacheState {
