@@ -125,6 +125,8 @@ def main():
     vs = [dev(w.v_new(n)) for n in range(NFE)]
     outs = [torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     lses = [torch.empty((H, w.n_q), dtype=torch.float32, device="cuda") for _ in range(L)]
+    ws_bytes = nm.nomas_attn_fwd_workspace_size(plans[0])
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
     n_cached_segs = len(w.cached)
@@ -136,7 +138,7 @@ def main():
                     e0, e1 = ev(), ev()
                     e0.record(stream)
                 nm.nomas_attn_fwd(plans[layer], caches[layer], qs[n], ks[n], vs[n], outs[layer],
-                                  lses[layer], D ** -0.5)
+                                  lses[layer], D ** -0.5, workspace=ws)
                 if fwd_events is not None:
                     e1.record(stream)
                     fwd_events.append((e0, e1))

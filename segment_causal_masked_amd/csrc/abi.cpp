@@ -61,6 +61,8 @@ struct nomas_plan {
   const nomas::KDescDev* d_kdesc = nullptr;
   const int32_t *d_csr_ptr = nullptr, *d_csr_idx = nullptr;
   const int32_t *d_csc_ptr = nullptr, *d_csc_idx = nullptr;
+  const int32_t* d_wg_ptr = nullptr;
+  const int4 *d_pieces = nullptr, *d_combine = nullptr;
 };
 
 namespace {
@@ -168,46 +170,59 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->cache_nseg = (int32_t)cache->segs.size();
     p->cache_last_serial = cache->serials.empty() ? 0 : cache->serials.back();
   }
+  int groups = 256 * nomas::attn_fwd_groups_per_cu();  // host-only plans: MI355X's 256 CUs
+  if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
+    hipError_t e = hipGetDevice(&p->device);
+    int cus = 0;
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "device query");
+    }
+    groups = cus * nomas::attn_fwd_groups_per_cu();
+  }
+  nomas::build_fwd_schedule(&p->host, groups);
   if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
     const nomas::HostPlan& h = p->host;
-    auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
-    const size_t b_q = al(h.qdesc.size() * sizeof(nomas::QDesc));
-    const size_t b_k = al(h.kdesc.size() * sizeof(nomas::KDesc));
-    const size_t b_rp = al(h.csr_ptr.size() * 4), b_ri = al(h.csr_idx.size() * 4 + 4);
-    const size_t b_cp = al(h.csc_ptr.size() * 4), b_ci = al(h.csc_idx.size() * 4 + 4);
-    const size_t total = b_q + b_k + b_rp + b_ri + b_cp + b_ci;
-    hipError_t e = hipGetDevice(&p->device);
-    if (e == hipSuccess) e = hipMalloc(&p->dmem, total);
+    struct Part { const void* src; size_t bytes; size_t off; };
+    Part parts[] = {{h.qdesc.data(), h.qdesc.size() * sizeof(nomas::QDesc), 0},
+                    {h.kdesc.data(), h.kdesc.size() * sizeof(nomas::KDesc), 0},
+                    {h.csr_ptr.data(), h.csr_ptr.size() * 4, 0},
+                    {h.csr_idx.data(), h.csr_idx.size() * 4, 0},
+                    {h.csc_ptr.data(), h.csc_ptr.size() * 4, 0},
+                    {h.csc_idx.data(), h.csc_idx.size() * 4, 0},
+                    {h.wg_ptr.data(), h.wg_ptr.size() * 4, 0},
+                    {h.pieces.data(), h.pieces.size() * sizeof(nomas::Piece), 0},
+                    {h.combine.data(), h.combine.size() * sizeof(nomas::CombineItem), 0}};
+    size_t total = 0;
+    for (Part& part : parts) {
+      part.off = total;
+      total += (part.bytes + 16 + 255) & ~size_t(255);  // >= 16 B slack, 256-B aligned
+    }
+    hipError_t e = hipMalloc(&p->dmem, total);
     if (e != hipSuccess) {
       delete p;
       return hip_fail(e, "plan upload");
     }
-    char* base = static_cast<char*>(p->dmem);
-    struct Part { const void* src; size_t bytes; size_t room; };
-    const Part parts[] = {{h.qdesc.data(), h.qdesc.size() * sizeof(nomas::QDesc), b_q},
-                          {h.kdesc.data(), h.kdesc.size() * sizeof(nomas::KDesc), b_k},
-                          {h.csr_ptr.data(), h.csr_ptr.size() * 4, b_rp},
-                          {h.csr_idx.data(), h.csr_idx.size() * 4, b_ri},
-                          {h.csc_ptr.data(), h.csc_ptr.size() * 4, b_cp},
-                          {h.csc_idx.data(), h.csc_idx.size() * 4, b_ci}};
     std::vector<char> staging(total, 0);
-    size_t off = 0;
-    for (const Part& part : parts) {
-      if (part.bytes) std::memcpy(staging.data() + off, part.src, part.bytes);
-      off += part.room;
-    }
+    for (const Part& part : parts)
+      if (part.bytes) std::memcpy(staging.data() + part.off, part.src, part.bytes);
     e = hipMemcpy(p->dmem, staging.data(), total, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(p->dmem);
       delete p;
       return hip_fail(e, "plan upload");
     }
-    p->d_qdesc = reinterpret_cast<const nomas::QDescDev*>(base);
-    p->d_kdesc = reinterpret_cast<const nomas::KDescDev*>(base + b_q);
-    p->d_csr_ptr = reinterpret_cast<const int32_t*>(base + b_q + b_k);
-    p->d_csr_idx = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp);
-    p->d_csc_ptr = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp + b_ri);
-    p->d_csc_idx = reinterpret_cast<const int32_t*>(base + b_q + b_k + b_rp + b_ri + b_cp);
+    char* base = static_cast<char*>(p->dmem);
+    p->d_qdesc = reinterpret_cast<const nomas::QDescDev*>(base + parts[0].off);
+    p->d_kdesc = reinterpret_cast<const nomas::KDescDev*>(base + parts[1].off);
+    p->d_csr_ptr = reinterpret_cast<const int32_t*>(base + parts[2].off);
+    p->d_csr_idx = reinterpret_cast<const int32_t*>(base + parts[3].off);
+    p->d_csc_ptr = reinterpret_cast<const int32_t*>(base + parts[4].off);
+    p->d_csc_idx = reinterpret_cast<const int32_t*>(base + parts[5].off);
+    p->d_wg_ptr = reinterpret_cast<const int32_t*>(base + parts[6].off);
+    p->d_pieces = reinterpret_cast<const int4*>(base + parts[7].off);
+    p->d_combine = reinterpret_cast<const int4*>(base + parts[8].off);
     p->on_device = true;
   }
   *out = p;
@@ -255,7 +270,7 @@ nomas_status nomas_plan_destroy(nomas_plan* p) {
 
 nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  *bytes = 0;
+  *bytes = (size_t)p->host.n_slots * nomas::attn_fwd_slot_bytes();
   return ok();
 }
 
@@ -264,8 +279,6 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
                             int64_t kv_stride, void* o, int64_t o_stride, float* lse,
                             float scale, void* workspace, size_t workspace_bytes,
                             void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!p->on_device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "host-only plan cannot run");
   if (!plan_matches_cache(p, cache))
@@ -283,6 +296,10 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
     return s;
   if (has_new && (s = check_stride(kv_stride, h.heads, "kv"))) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  size_t need = (size_t)h.n_slots * nomas::attn_fwd_slot_bytes();
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "workspace missing or smaller than nomas_attn_fwd_workspace_size");
+  if ((s = check_dev_ptr(workspace, need > 0, "workspace"))) return s;
   if ((s = check_device(p))) return s;
 
   nomas::FwdParams fp{};
@@ -297,6 +314,12 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
   fp.kdesc = p->d_kdesc;
   fp.csr_ptr = p->d_csr_ptr;
   fp.csr_idx = p->d_csr_idx;
+  fp.wg_ptr = p->d_wg_ptr;
+  fp.pieces = p->d_pieces;
+  fp.combine = p->d_combine;
+  fp.partial = static_cast<float*>(workspace);
+  fp.groups = h.fwd_groups;
+  fp.n_combine = (int32_t)h.combine.size();
   fp.q_stride = q_stride;
   fp.kv_stride = kv_stride;
   fp.o_stride = o_stride;

@@ -28,12 +28,19 @@ struct FwdParams {
   const KDescDev* kdesc;   // nkt*64 entries
   const int32_t* csr_ptr;  // nqt+1
   const int32_t* csr_idx;  // (k_tile << 1) | needs_mask
+  const int32_t* wg_ptr;   // groups+1: pieces of each persistent workgroup
+  const int4* pieces;      // {unit, entry_begin, entry_end, slot or -1}
+  const int4* combine;     // {unit, first_slot, n_pieces, 0}
+  float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
   int64_t q_stride, kv_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;
+  int32_t groups, n_combine;
   float scale_log2;        // softmax scale * log2(e)
 };
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
+size_t attn_fwd_slot_bytes();
+int attn_fwd_groups_per_cu();  // persistent forward workgroups per CU
 
 struct AppendParams {
   const uint16_t* k_src;   // [T][H][128], stride src_stride

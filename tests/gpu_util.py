@@ -68,9 +68,14 @@ def fill_cache(cache, segments, k_tok, v_tok):
     return off
 
 
+def fwd_workspace(plan):
+    n = nm.nomas_attn_fwd_workspace_size(plan)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda") if n else None
+
+
 def run_fwd(plan, cache, q, k_new, v_new, heads, lse=True):
     o = torch.empty((q.shape[0], heads, 128), dtype=torch.bfloat16, device="cuda")
     l = torch.empty((heads, q.shape[0]), dtype=torch.float32, device="cuda") if lse else None
-    nm.nomas_attn_fwd(plan, cache, q, k_new, v_new, o, l, SCALE)
+    nm.nomas_attn_fwd(plan, cache, q, k_new, v_new, o, l, SCALE, workspace=fwd_workspace(plan))
     torch.cuda.synchronize()
     return o, l

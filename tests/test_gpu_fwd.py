@@ -182,6 +182,11 @@ def test_single_token_and_empty_query():
     plan0 = nm.nomas_attn_plan([], s1, heads=2)
     o0 = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
     nm.nomas_attn_fwd(plan0, None, o0, q, q, o0, None, SCALE)
+    # a plan whose queries see nothing at all (padding only): zeros and -inf
+    sp = [wl.Segment(0, 0, 0, 0, 0, [], n_pad=200)]
+    qp = dev(wl.randn((200, 2, 128), 6))
+    o_p, l_p = run_fwd(nm.nomas_attn_plan(sp, sp, heads=2), None, qp, qp, qp, 2)
+    assert (o_p == 0).all() and torch.isinf(l_p).all() and (l_p < 0).all()
     torch.cuda.synchronize()
 
 
