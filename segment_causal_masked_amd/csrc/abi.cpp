@@ -63,6 +63,7 @@ struct nomas_plan {
   const int32_t *d_csc_ptr = nullptr, *d_csc_idx = nullptr;
   const int32_t* d_wg_ptr = nullptr;
   const int4 *d_pieces = nullptr, *d_combine = nullptr;
+  const int32_t *d_pair_ptr = nullptr, *d_pair_idx = nullptr;
 };
 
 namespace {
@@ -193,7 +194,9 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
                     {h.csc_idx.data(), h.csc_idx.size() * 4, 0},
                     {h.wg_ptr.data(), h.wg_ptr.size() * 4, 0},
                     {h.pieces.data(), h.pieces.size() * sizeof(nomas::Piece), 0},
-                    {h.combine.data(), h.combine.size() * sizeof(nomas::CombineItem), 0}};
+                    {h.combine.data(), h.combine.size() * sizeof(nomas::CombineItem), 0},
+                    {h.pair_ptr.data(), h.pair_ptr.size() * 4, 0},
+                    {h.pair_idx.data(), h.pair_idx.size() * 4, 0}};
     size_t total = 0;
     for (Part& part : parts) {
       part.off = total;
@@ -223,6 +226,8 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->d_wg_ptr = reinterpret_cast<const int32_t*>(base + parts[6].off);
     p->d_pieces = reinterpret_cast<const int4*>(base + parts[7].off);
     p->d_combine = reinterpret_cast<const int4*>(base + parts[8].off);
+    p->d_pair_ptr = reinterpret_cast<const int32_t*>(base + parts[9].off);
+    p->d_pair_idx = reinterpret_cast<const int32_t*>(base + parts[10].off);
     p->on_device = true;
   }
   *out = p;
@@ -312,8 +317,9 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
   fp.lse = lse;
   fp.qdesc = p->d_qdesc;
   fp.kdesc = p->d_kdesc;
-  fp.csr_ptr = p->d_csr_ptr;
-  fp.csr_idx = p->d_csr_idx;
+  fp.csr_ptr = p->d_pair_ptr;
+  fp.csr_idx = p->d_pair_idx;
+  fp.n_pairs = (int32_t)h.n_pairs;
   fp.wg_ptr = p->d_wg_ptr;
   fp.pieces = p->d_pieces;
   fp.combine = p->d_combine;

@@ -8,10 +8,15 @@
 // Online softmax keeps a running max and sum per query in fp32, so the result
 // equals the plain softmax up to rounding.
 //
-// Scheduling (persistent, stream-K style): the host cuts the (unit, key tile)
-// iterations, unit = head * n_q_tiles + q_tile, into equal contiguous ranges,
-// one per workgroup (two workgroups of four waves per CU, so each SIMD runs two
-// waves that hide each other's latencies).  A unit split between ranges is
+// Scheduling (persistent, stream-K style): a unit is a pair of consecutive
+// 128-query tiles of one head (256 queries, one per lane column of the eight
+// waves of a workgroup, two waves per SIMD); its key tiles are the union of the
+// pair's tile lists, with per-q-tile EMPTY / mask flags.  The host cuts the
+// (unit, key tile) iterations into equal contiguous ranges, one per workgroup
+// (one per CU).  Each K/V tile fetched serves 256 queries, and the 130 KB of
+// LDS hold four tile stages used as two pairs: a pair of tiles is computed
+// while the next pair loads, with one barrier per pair.  A unit
+// split between ranges is
 // computed in pieces whose un-normalised (O, max, sum) go to a workspace and
 // are merged by attn_fwd_combine_kernel.  Workgroup ids are remapped so that
 // the workgroups of one XCD take consecutive ranges, i.e. the q-tiles of the
@@ -54,10 +59,12 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 typedef __attribute__((address_space(3))) i16x4* lds_i16x4p;
 
 constexpr int D = 128;
-constexpr int BQ = 128;
 constexpr int BK = 64;
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
+constexpr int UNIT_ROWS = 32 * NWAVES;  // 256 queries: a pair of 128-query tiles
+constexpr int NSTAGE = 4;
+constexpr int LOADS_PER_TILE = 4;       // per wave: 2 K + 2 V blocks (wave 0: + descriptors)
 constexpr int TILE_BYTES = BK * D * 2;  // 16 KB: one K or V tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr float RESCALE_SLACK = 8.0f;
@@ -103,10 +110,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt untouched): N in [0, 63].
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Everything the tile loads need, copied out of the kernel arguments.
-// Load i of wave w fills LDS block 4 i + w of a tile: rows 16 w .. 16 w + 15,
-// chunks 4 i .. 4 i + 3.  Lane l fetches row 16 w + l / 4, chunk
-// 4 i + ((l % 4) ^ ((l / 16) % 4)): its offset inside a tile is constant.
+// Wave w fills LDS blocks (chunk group w / 4 + 2 i, rows 16 (w % 4) ..+15) of
+// a tile for i = 0, 1.  Lane l fetches row 16 (w % 4) + l / 4 and chunk
+// 4 (w / 4 + 2 i) + ((l % 4) ^ ((l / 16) % 4)): its offset inside a tile is
+// constant up to the scalar 32 (w / 4 + 2 i).
 struct LoadCtx {
   const uint16_t *k_cache_h, *v_cache_h;  // head h's rows in the cache
   const uint16_t *k_new_h, *v_new_h;      // head h's column in the new-token rows
@@ -119,24 +134,22 @@ struct LoadCtx {
 __device__ __forceinline__ void issue_half(const LoadCtx& c, const uint16_t* cache_h,
                                            const uint16_t* new_h, char* dst, int kt, int w) {
   const int k0 = kt * BK;
-  char* d = dst + 1024 * w;
+  const int gq = w >> 2;
+  char* d = dst + 4096 * gq + 1024 * (w & 3);
+  const uint16_t* src;
   if (k0 + BK <= c.n_cached) {
-    const uint16_t* src = cache_h + (int64_t)k0 * D + c.lane_cache;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src + 32 * i, d + 4096 * i);
+    src = cache_h + (int64_t)k0 * D + c.lane_cache;
   } else if (k0 >= c.n_cached && k0 + BK <= c.nk) {
-    const uint16_t* src = new_h + (int64_t)(k0 - c.n_cached) * c.kv_stride + c.lane_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src + 32 * i, d + 4096 * i);
+    src = new_h + (int64_t)(k0 - c.n_cached) * c.kv_stride + c.lane_new;
   } else {  // straddles the cache / new boundary or runs past the last key
     int key = k0 + c.lane_row;
     key = key < c.nk ? key : c.nk - 1;  // any valid row: masked later
-    const uint16_t* src = key < c.n_cached ? cache_h + (int64_t)key * D
-                                           : new_h + (int64_t)(key - c.n_cached) * c.kv_stride;
-    src += 8 * c.lane_chunk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src + 32 * i, d + 4096 * i);
+    src = (key < c.n_cached ? cache_h + (int64_t)key * D
+                            : new_h + (int64_t)(key - c.n_cached) * c.kv_stride) + 8 * c.lane_chunk;
   }
+  src += 32 * gq;
+  dma16(src, d);
+  dma16(src + 64, d + 8192);
 }
 
 struct WaveState {
@@ -175,16 +188,17 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
         s[kb][ri] = visible(ws.qd, d.seg, d.bits) ? s[kb][ri] : -INFINITY;
       }
   }
-  // this half-wave's max over its 32 keys (tree)
-  float t[11];
+  // this half-wave's max over its 32 keys: a 16-op max3 tree
+  float t[12];
 #pragma unroll
   for (int j = 0; j < 5; ++j) t[j] = fmaxf(fmaxf(s[0][3 * j], s[0][3 * j + 1]), s[0][3 * j + 2]);
 #pragma unroll
   for (int j = 0; j < 5; ++j) t[5 + j] = fmaxf(fmaxf(s[1][3 * j], s[1][3 * j + 1]), s[1][3 * j + 2]);
-  t[10] = fmaxf(s[0][15], s[1][15]);
-  float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
-                   fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-  mx = fmaxf(mx, fmaxf(fmaxf(t[8], t[9]), t[10]));
+  t[10] = s[0][15];
+  t[11] = s[1][15];
+  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(fmaxf(t[9], t[10]), t[11]);
+  const float mx = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
   const float m_half = mx * scale_log2;
   // Raise the reference max only when a row's tile max exceeds it by more than
   // RESCALE_SLACK; the decision is per row (both halves agree after the
@@ -201,6 +215,8 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   }
   const float m_use = ws.m_run == -INFINITY ? 0.f : ws.m_run;
 
+  // P = exp2(s * scale_log2 - m) in fp32, summed in fp32 (four chains) and
+  // rounded to bf16 as the operand of the P.V product.
   bf16x8 pf[4];  // P^T operand for step (kb, half) = 2 kb + half
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -257,26 +273,33 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const f32x16* acc,
         l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
 }
 
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
-  // Two stage buffers (K | V of one tile) and their key descriptors.
+__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(FwdParams p) {
+  // Four stage buffers (K | V of one tile) and their key descriptors, as
+  // distinct LDS objects.
   __shared__ __attribute__((aligned(1024))) char sbuf0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sbuf1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbuf2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbuf3[STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) KDescDev skd0[BK];
   __shared__ __attribute__((aligned(16))) KDescDev skd1[BK];
+  __shared__ __attribute__((aligned(16))) KDescDev skd2[BK];
+  __shared__ __attribute__((aligned(16))) KDescDev skd3[BK];
+  static_assert(NSTAGE == 4, "the unrolled loop below names four stage buffers");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31;   // query column of this lane
   const int hh = lane >> 5;   // half-wave
+  const int half = w >> 2;    // which q-tile of the pair this wave serves
 
   // logical workgroup: XCD-major (dispatch places workgroup b on XCD b % 8)
   const int G = (int)gridDim.x;
   const int g = (G & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
 
-  const const_i32p csr_ptr = (const_i32p)p.csr_ptr;
-  const const_i32p csr_idx = (const_i32p)p.csr_idx;
-  const const_i32p pieces = (const_i32p)p.pieces;  // 4 ints per piece
+  const const_i32p unit_ptr = (const_i32p)p.csr_ptr;   // merged lists per q-tile pair
+  const const_i32p unit_idx = (const_i32p)p.csr_idx;
+  const const_i32p pieces = (const_i32p)p.pieces;     // 4 ints per piece
   const int pc0 = ((const_i32p)p.wg_ptr)[g], pc1 = ((const_i32p)p.wg_ptr)[g + 1];
   const float scale_log2 = p.scale_log2;
 
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   lc.kv_stride = p.kv_stride;
   lc.nk = p.nk;
   lc.n_cached = p.n_cached;
-  lc.lane_row = 16 * w + (lane >> 2);
+  lc.lane_row = 16 * (w & 3) + (lane >> 2);
   lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
   lc.lane_cache = lc.lane_row * D + 8 * lc.lane_chunk;
   lc.lane_new = (int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk;
@@ -304,10 +327,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   for (int pc = pc0; pc < pc1; ++pc) {
     const int unit = pieces[4 * pc];
     const int e_begin = pieces[4 * pc + 1], e_end = pieces[4 * pc + 2], slot = pieces[4 * pc + 3];
-    const int h = unit / p.nqt;
-    const int qt = unit - h * p.nqt;
-    const int qrow = qt * BQ + w * 32 + jq;
-    const const_i32p ent = csr_idx + csr_ptr[qt] + e_begin;
+    const int h = unit / p.n_pairs;
+    const int pr = unit - h * p.n_pairs;
+    const int qrow = pr * UNIT_ROWS + w * 32 + jq;
+    const const_i32p ent = unit_idx + unit_ptr[pr] + e_begin;
     const int n_ent = e_end - e_begin;
     lc.k_cache_h = p.k_cache + (int64_t)h * p.cache_cap * D;
     lc.v_cache_h = p.v_cache + (int64_t)h * p.cache_cap * D;
@@ -322,7 +345,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8) ws.qf[s8] = bf16x8{};
     }
-    ws.qd = p.qdesc[qrow];  // padded to whole tiles
+    // the query descriptors are padded to whole 128-query tiles; a missing
+    // second tile of the last pair reads the padding of the first tile's end
+    ws.qd = qrow < p.nqt * 128 ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
 #pragma unroll
     for (int db = 0; db < 4; ++db) ws.acc[db] = f32x16{};
     ws.m_run = -INFINITY;
@@ -332,24 +357,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     // would also drain the tile prefetches issued below.
     wait_vm_all();
 
-    auto issue_tile = [&](int kt, char* buf, KDescDev* kd) {
+    auto issue_tile = [&](int e, char* buf, KDescDev* kd) {
+      const int kt = ent[e] >> 4;
       issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
       issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
       if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
     };
-    if (n_ent > 0) issue_tile(ent[0] >> 1, sbuf0, skd0);
+    if (n_ent > 0) issue_tile(0, sbuf0, skd0);
+    if (n_ent > 1) issue_tile(1, sbuf1, skd1);
 
-    // tile t computes from buffer t & 1 while tile t + 1 loads into the other
-    auto body = [&](int t, const char* cbuf, const KDescDev* ckd, char* nbuf, KDescDev* nkd) {
-      wait_vm_all();   // this wave's loads of tile t (the only ones in flight)
-      lds_barrier();   // ... and every other wave's; tile t-1 fully consumed
+    // Tiles go in pairs: iteration j computes tiles 2j, 2j+1 (buffers of one
+    // half of the ring) after issuing tiles 2j+2, 2j+3 into the other half,
+    // which the barrier has just released; one barrier per two tiles.
+    auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) {
       const int here = ent[t];
-      if (t + 1 < n_ent) issue_tile(ent[t + 1] >> 1, nbuf, nkd);
-      tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, here & 1, scale_log2, hh);
+      if (!((here >> (2 + half)) & 1))  // not EMPTY for this wave's q-tile
+        tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, (here >> half) & 1, scale_log2, hh);
     };
-    for (int t = 0; t < n_ent; t += 2) {
-      body(t, sbuf0, skd0, sbuf1, skd1);
-      if (t + 1 < n_ent) body(t + 1, sbuf1, skd1, sbuf0, skd0);
+    auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
+                    char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {
+      wait_vm_all();  // this wave's loads of tiles t, t+1 (the only ones in flight)
+      lds_barrier();  // ... and every other wave's; tiles t-2, t-1 fully consumed
+      if (t + 2 < n_ent) issue_tile(t + 2, n0, nk0);
+      if (t + 3 < n_ent) issue_tile(t + 3, n1, nk1);
+      tile(t, b0, k0);
+      if (t + 1 < n_ent) tile(t + 1, b1, k1);
+    };
+    for (int t = 0; t < n_ent; t += 4) {
+      pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
+      if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, sbuf0, skd0, sbuf1, skd1);
     }
 
     if (slot < 0) {
@@ -364,22 +400,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
       dst[64 * NTHREADS] = ws.m_run;
       dst[65 * NTHREADS] = ws.l_run;
     }
+    wait_vm_all();  // stores retired before the next piece's load accounting
     lds_barrier();  // the stage buffers are reused by the next piece
   }
 }
 
 // Merge the pieces of split units: O = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k.
-// Workgroup (item, db) handles dims 32 db .. 32 db + 31 of one split unit's
-// 128 rows; thread T mirrors thread T of the forward workgroup.
-__global__ __launch_bounds__(NTHREADS) void attn_fwd_combine_kernel(FwdParams p) {
-  const const_i32p cmb = (const_i32p)p.combine + 4 * (blockIdx.x >> 2);
-  const int db = blockIdx.x & 3;
+// Workgroup (item, db, r) handles dims 32 db .. 32 db + 31 of rows 128 r ..
+// 128 r + 127 of one split unit; thread T mirrors forward thread 256 r + T.
+__global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
+  const const_i32p cmb = (const_i32p)p.combine + 4 * (blockIdx.x >> 3);
+  const int db = (blockIdx.x >> 1) & 3, r = blockIdx.x & 1;
   const int unit = cmb[0], first = cmb[1], n = cmb[2];
-  const int h = unit / p.nqt;
-  const int qt = unit - h * p.nqt;
-  const int T = threadIdx.x;
+  const int h = unit / p.n_pairs;
+  const int pr = unit - h * p.n_pairs;
+  const int T = 256 * r + (int)threadIdx.x;
   const int lane = T & 63;
-  const int qrow = qt * BQ + (T >> 6) * 32 + (lane & 31);
+  const int qrow = pr * UNIT_ROWS + (T >> 6) * 32 + (lane & 31);
   const int hh = lane >> 5;
   const float* base = p.partial + (int64_t)first * SLOT_FLOATS + T;
   float m = -INFINITY;
@@ -401,14 +438,14 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_combine_kernel(FwdParams p)
 }  // namespace
 
 size_t attn_fwd_slot_bytes() { return (size_t)SLOT_FLOATS * sizeof(float); }
-int attn_fwd_groups_per_cu() { return 2; }
+int attn_fwd_groups_per_cu() { return 1; }
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.nq == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)p.groups), dim3(NTHREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;
-  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3((unsigned)(4 * p.n_combine)), dim3(NTHREADS), 0,
+  hipLaunchKernelGGL(attn_fwd_combine_kernel, dim3((unsigned)(8 * p.n_combine)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }

@@ -26,15 +26,15 @@ struct FwdParams {
   float* lse;              // [H][nq] or null
   const QDescDev* qdesc;   // nqt*128 entries
   const KDescDev* kdesc;   // nkt*64 entries
-  const int32_t* csr_ptr;  // nqt+1
-  const int32_t* csr_idx;  // (k_tile << 1) | needs_mask
+  const int32_t* csr_ptr;  // per q-tile pair: n_pairs+1
+  const int32_t* csr_idx;  // (k_tile << 4) | flags (see plan.h)
   const int32_t* wg_ptr;   // groups+1: pieces of each persistent workgroup
   const int4* pieces;      // {unit, entry_begin, entry_end, slot or -1}
   const int4* combine;     // {unit, first_slot, n_pieces, 0}
   float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
   int64_t q_stride, kv_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;
-  int32_t groups, n_combine;
+  int32_t groups, n_combine, n_pairs;
   float scale_log2;        // softmax scale * log2(e)
 };
 

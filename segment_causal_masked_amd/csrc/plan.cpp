@@ -9,6 +9,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
 #include <map>
 #include <tuple>
 #include <utility>
@@ -288,8 +289,30 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
 
 void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   HostPlan& p = *pp;
-  const int64_t n_units = int64_t(p.heads) * p.nqt;
-  const int64_t row_total = p.csr_ptr.empty() ? 0 : p.csr_ptr.back();
+  // merged entry lists of q-tile pairs
+  p.n_pairs = (p.nqt + 1) / 2;
+  p.pair_ptr.assign(size_t(p.n_pairs + 1), 0);
+  p.pair_idx.clear();
+  for (int64_t u = 0; u < p.n_pairs; ++u) {
+    const int64_t qa = 2 * u, qb = 2 * u + 1;
+    int32_t ia = p.csr_ptr[size_t(qa)], ea = p.csr_ptr[size_t(qa + 1)];
+    int32_t ib = qb < p.nqt ? p.csr_ptr[size_t(qb)] : 0, eb = qb < p.nqt ? p.csr_ptr[size_t(qb + 1)] : 0;
+    while (ia < ea || ib < eb) {
+      const int32_t ka = ia < ea ? (p.csr_idx[size_t(ia)] >> 1) : INT32_MAX;
+      const int32_t kb = ib < eb ? (p.csr_idx[size_t(ib)] >> 1) : INT32_MAX;
+      const int32_t kt = std::min(ka, kb);
+      int32_t flags = 0;
+      if (ka == kt) flags |= (p.csr_idx[size_t(ia++)] & 1);
+      else flags |= 4;  // EMPTY for the first q-tile
+      if (kb == kt) flags |= (p.csr_idx[size_t(ib++)] & 1) << 1;
+      else flags |= 8;  // EMPTY for the second q-tile (or it does not exist)
+      p.pair_idx.push_back((kt << 4) | flags);
+    }
+    p.pair_ptr[size_t(u + 1)] = int32_t(p.pair_idx.size());
+  }
+
+  const int64_t n_units = int64_t(p.heads) * p.n_pairs;
+  const int64_t row_total = p.pair_ptr.back();
   const int64_t total = int64_t(p.heads) * row_total;
   groups = std::max<int32_t>(1, groups);
   p.fwd_groups = groups;
@@ -305,26 +328,25 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     return std::min<int64_t>(g, groups - 1);
   };
   for (int64_t u = 0; u < n_units; ++u) {
-    const int64_t h = u / p.nqt, qt = u % p.nqt;
-    const int64_t n = p.csr_ptr[size_t(qt + 1)] - p.csr_ptr[size_t(qt)];
-    const int64_t start = h * row_total + p.csr_ptr[size_t(qt)];
+    const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
+    const int64_t n = p.pair_ptr[size_t(pr + 1)] - p.pair_ptr[size_t(pr)];
+    const int64_t start = h * row_total + p.pair_ptr[size_t(pr)];
     if (n == 0) {  // nothing visible: still owes zeros / -inf to its rows
       per[size_t(group_of(std::min(start, std::max<int64_t>(total - 1, 0))))].push_back(
           Piece{int32_t(u), 0, 0, -1});
       continue;
     }
     const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
-    const int32_t first_slot = p.n_slots;
     for (int64_t g = g0; g <= g1; ++g) {
       const int64_t a = std::max(bound(g), start), b = std::min(bound(g + 1), start + n);
       if (a >= b) continue;
       per[size_t(g)].push_back(Piece{int32_t(u), int32_t(a - start), int32_t(b - start), -1});
     }
-    // count the pieces actually made (ranges of zero width were skipped)
     int32_t made = 0;
     for (int64_t g = g0; g <= g1; ++g)
       if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u)) ++made;
     if (made > 1) {
+      const int32_t first_slot = p.n_slots;
       for (int64_t g = g0; g <= g1; ++g)
         if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u))
           per[size_t(g)].back().slot = p.n_slots++;

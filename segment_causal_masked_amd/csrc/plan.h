@@ -36,9 +36,12 @@ inline bool visible(const QDesc& q, const KDesc& k) {
          (k.bits == 0u || (k.seg == q.seg && (q.amask & k.bits) != 0u));
 }
 
-// Forward work schedule.  The iterations of the forward are (unit, entry)
-// pairs, unit = head * n_q_tiles + q_tile, entry = position in the q-tile's
-// list of non-empty key tiles.  They are cut into `groups` contiguous,
+// Forward work schedule.  A forward unit is a pair of consecutive query tiles
+// (q-tiles 2 u' and 2 u' + 1) of one head: unit = head * n_pairs + u'.  Its
+// entries are the union of the two q-tiles' non-empty key tiles, each entry
+// = (k_tile << 4) | flags: bit 0 / 1 = the first / second q-tile needs the
+// per-element mask there, bit 2 / 3 = the tile is EMPTY for the first /
+// second q-tile (its waves skip it).  The iterations (unit, entry)  They are cut into `groups` contiguous,
 // equal ranges, one per persistent workgroup; a unit cut by a range boundary
 // becomes several pieces whose partial results are merged afterwards.
 struct Piece {
@@ -62,6 +65,8 @@ struct HostPlan {
   int64_t n_empty = 0, n_full = 0, n_partial = 0;
   int64_t unmasked_pairs = 0, executed_pairs = 0;
   // forward schedule (build_fwd_schedule)
+  int64_t n_pairs = 0;                // ceil(nqt / 2)
+  std::vector<int32_t> pair_ptr, pair_idx;  // merged entry lists per q-tile pair
   int32_t fwd_groups = 0;
   std::vector<int32_t> wg_ptr;        // fwd_groups + 1
   std::vector<Piece> pieces;
