@@ -11,9 +11,11 @@ layer's cache.  The host plan is built once per segment step and shared by all
 layers and calls; its time is reported separately.
 
 value = 4 * 128 * 16 * A * (4 calls * L layers) / step time, A = unmasked pairs.
-roofline = the forward kernel: the same effective FLOPs per launch / the
-launch's average duration (HIP events on the launch stream), against the bf16
-dense MFMA peak of MI355X.
+roofline = one forward call (the persistent forward kernel plus the small
+kernel that merges split query tiles, back to back on one stream): the same
+effective FLOPs per call / the call's average duration (HIP events on the
+launch stream), against the bf16 dense MFMA peak of MI355X.
+cpu_baseline = the fp64 oracle on one forward call of the same workload.
 """
 from __future__ import annotations
 
@@ -34,8 +36,12 @@ PEAK_HBM_GBS = 8000.0
 
 
 def kernel_hash():
-    src = os.path.join(ROOT, "segment_causal_masked_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of the sources that decide the forward's HBM traffic (kernel and
+    host schedule)."""
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "plan.cpp"):
+        h.update(open(os.path.join(ROOT, "segment_causal_masked_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload):
@@ -51,8 +57,20 @@ def traffic_from_profiles(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, heads=4):
-    """The fp64 oracle on a bounded sample of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w):
+    """The fp64 oracle (numpy, BLAS threads = this process's cores) on one full
+    forward call of the same workload: all 16 heads, every query of the new
+    segment against all cached + new keys."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -62,18 +80,20 @@ def cpu_baseline(w, heads=4):
         cores = len(os.sched_getaffinity(0))
     keys = w.cached + w.new
     kc, vc = w.cache_kv()
-    q = w.q()[:, :heads]
-    k = np.concatenate([kc, w.k_new()])[:, :heads]
-    v = np.concatenate([vc, w.v_new()])[:, :heads]
+    q = w.q()
+    k = np.concatenate([kc, w.k_new()])
+    v = np.concatenate([vc, w.v_new()])
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
     t0 = time.perf_counter()
     oracle.forward(q, k, v, tq, tk, 128 ** -0.5)
     dt = time.perf_counter() - t0
     a = oracle.unmasked_pairs(tq, tk)
-    flop = 4.0 * 128 * heads * a
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{w.name}: {heads} of 16 heads, all {w.n_q} queries x {w.n_keys} keys, "
-                      f"fp64 numpy, {dt:.1f} s"}
+    flop = 4.0 * 128 * w.heads * a
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"one forward call of {w.name} ({w.heads} heads, {w.n_q} queries x "
+                      f"{w.n_keys} keys), fp64 numpy, single run: {dt:.1f} s",
+            "cpu": cpu_model()}
 
 
 def main():
@@ -83,6 +103,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (untimed), as a known "
+                         "quantity for calibrating HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -155,6 +178,15 @@ def main():
         for c in caches:
             nm.nomas_kvcache_truncate(c, n_cached_segs)
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -205,6 +237,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
         "fwd_ms_per_call": round(fwd_avg, 4),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
+        "fwd_calls_timed": int(fwd_ms.size),
         "fwd_ms_min": round(float(fwd_ms.min()), 4),
         "executed_over_effective": round(info.executed_pairs / A, 4),
         "append_ms": round(float(app_ms.mean()), 4),

@@ -77,9 +77,12 @@ __device__ __forceinline__ int kmap(int i) {
   return 16 * (g >> 1) + 8 * q + 4 * (g & 1) + r;
 }
 
+// Branch-free (bitwise, not short-circuit), so that masking compiles to
+// compares and selects on the score registers in place.
 __device__ __forceinline__ bool visible(const QDescDev& q, int kseg, uint32_t kbits) {
-  return kseg >= q.lo && kseg <= q.seg &&
-         (kbits == 0u || (kseg == q.seg && (q.amask & kbits) != 0u));
+  const bool in_range = (kseg >= q.lo) & (kseg <= q.seg);
+  const bool tail_ok = (kseg == q.seg) & ((q.amask & kbits) != 0u);
+  return in_range & ((kbits == 0u) | tail_ok);
 }
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -166,18 +169,42 @@ struct WaveState {
 __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, const char* vtile,
                                           const KDescDev* kd, bool masked, float scale_log2,
                                           int hh) {
-  f32x16 s[2];
+  // S^T for keys 32 kb + (0..31): two independent accumulation chains,
+  // interleaved, with the K fragments read four MFMAs ahead.
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  auto kfrag = [&](int i) {  // i = 2 ks + kb: row 32 kb + kmap(jq), chunk 2 ks + hh
+    const int kb = i & 1, ks = i >> 1;
+    return *reinterpret_cast<const bf16x8*>(ktile + ws.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
+  };
+  bf16x8 kf[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = f32x16{};
+  for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      // row 32 kb + kmap(jq), chunk 2 ks + hh
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-          ktile + ws.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, ws.qf[ks], s[kb], 0, 0, 0);
-    }
+  for (int i = 0; i < 16; ++i) {
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], ws.qf[i >> 1], s[i & 1], 0, 0, 0);
+    if (i + 4 < 16) kf[i & 3] = kfrag(i + 4);
   }
+  // keep that order: the scheduler would otherwise sink each read next to
+  // its MFMA and expose the LDS latency sixteen times
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+  // the first V^T fragments of O^T += V^T P^T, read now so that their
+  // latency hides under the softmax
+  auto vfrag = [&](int i) {  // i = 4 step + db: keys 16 step + 8 hh + (0..7), dims 32 db + ..
+    const char* a = vtile + 4096 * (i & 3) + 1024 * (i >> 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + ws.vbase[0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + ws.vbase[1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8 vf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vf[i] = vfrag(i);
   // register ri of block kb holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
   if (masked) {
 #pragma unroll
@@ -218,7 +245,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   // P = exp2(s * scale_log2 - m) in fp32, summed in fp32 (four chains) and
   // rounded to bf16 as the operand of the P.V product.
   bf16x8 pf[4];  // P^T operand for step (kb, half) = 2 kb + half
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  float lsum[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -228,7 +255,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
       for (int e8 = 0; e8 < 8; ++e8) {
         const float pe = __builtin_amdgcn_exp2f(
             __builtin_fmaf(s[kb][8 * half + e8], scale_log2, -m_use));
-        lsum[e8 & 3] += pe;
+        lsum[e8 & 3] = (kb | half | (e8 >> 2)) ? lsum[e8 & 3] + pe : pe;
         v[e8] = (__bf16)pe;
       }
       pf[2 * kb + half] = v;
@@ -236,17 +263,16 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   ws.l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
 #pragma unroll
-  for (int step = 0; step < 4; ++step) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      // keys 16 step + 8 hh + {0..3 | 4..7}, dims 32 db + 16 (lane/16 % 2) + 4 (lane % 4)
-      const char* a = vtile + 4096 * db + 1024 * step;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + ws.vbase[0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + ws.vbase[1]));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      ws.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[step], ws.acc[db], 0, 0, 0);
-    }
+  for (int i = 0; i < 16; ++i) {
+    ws.acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pf[i >> 2], ws.acc[i & 3], 0, 0, 0);
+    if (i + 4 < 16) vf[i & 3] = vfrag(i + 4);
   }
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of a fragment
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Normalise and store one lane's query row (O in bf16, LSE in natural log);
@@ -273,7 +299,7 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const f32x16* acc,
         l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
 }
 
-__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
   // Four stage buffers (K | V of one tile) and their key descriptors, as
   // distinct LDS objects.
   __shared__ __attribute__((aligned(1024))) char sbuf0[STAGE_BYTES];
