@@ -179,6 +179,9 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   bf16x8 kf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
+  // A wave issuing its MFMA block runs at raised priority, so that the other
+  // wave of the SIMD fills the gaps with its softmax instead of competing.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], ws.qf[i >> 1], s[i & 1], 0, 0, 0);
@@ -193,6 +196,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_s_setprio(0);
 
   // the first V^T fragments of O^T += V^T P^T, read now so that their
   // latency hides under the softmax
@@ -262,6 +266,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
     }
   ws.l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     ws.acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pf[i >> 2], ws.acc[i & 3], 0, 0, 0);
@@ -273,6 +278,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two reads of a fragment
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Normalise and store one lane's query row (O in bf16, LSE in natural log);
