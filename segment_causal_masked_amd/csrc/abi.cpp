@@ -64,6 +64,7 @@ struct nomas_plan {
   const int32_t* d_wg_ptr = nullptr;
   const int4 *d_pieces = nullptr, *d_combine = nullptr;
   const int32_t *d_pair_ptr = nullptr, *d_pair_idx = nullptr;
+  const int32_t *d_kpair_ptr = nullptr, *d_kpair_idx = nullptr;
 };
 
 namespace {
@@ -183,6 +184,7 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     groups = cus * nomas::attn_fwd_groups_per_cu();
   }
   nomas::build_fwd_schedule(&p->host, groups);
+  if (!p->has_cache) nomas::build_bwd_schedule(&p->host);
   if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
     const nomas::HostPlan& h = p->host;
     struct Part { const void* src; size_t bytes; size_t off; };
@@ -196,7 +198,9 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
                     {h.pieces.data(), h.pieces.size() * sizeof(nomas::Piece), 0},
                     {h.combine.data(), h.combine.size() * sizeof(nomas::CombineItem), 0},
                     {h.pair_ptr.data(), h.pair_ptr.size() * 4, 0},
-                    {h.pair_idx.data(), h.pair_idx.size() * 4, 0}};
+                    {h.pair_idx.data(), h.pair_idx.size() * 4, 0},
+                    {h.kpair_ptr.data(), h.kpair_ptr.size() * 4, 0},
+                    {h.kpair_idx.data(), h.kpair_idx.size() * 4, 0}};
     size_t total = 0;
     for (Part& part : parts) {
       part.off = total;
@@ -228,6 +232,8 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->d_combine = reinterpret_cast<const int4*>(base + parts[8].off);
     p->d_pair_ptr = reinterpret_cast<const int32_t*>(base + parts[9].off);
     p->d_pair_idx = reinterpret_cast<const int32_t*>(base + parts[10].off);
+    p->d_kpair_ptr = reinterpret_cast<const int32_t*>(base + parts[11].off);
+    p->d_kpair_idx = reinterpret_cast<const int32_t*>(base + parts[12].off);
     p->on_device = true;
   }
   *out = p;
@@ -348,7 +354,8 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
 
 nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  *bytes = (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
+  // delta and lse * log2(e) per (head, query row of the padded q-tiles)
+  *bytes = 2 * (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
   return ok();
 }
 
@@ -389,12 +396,13 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.dk = static_cast<uint16_t*>(dk);
   bp.dv = static_cast<uint16_t*>(dv);
   bp.delta = static_cast<float*>(workspace);
+  bp.lse2 = bp.delta + (size_t)h.heads * (size_t)h.nqt * 128;
   bp.qdesc = p->d_qdesc;
   bp.kdesc = p->d_kdesc;
-  bp.csr_ptr = p->d_csr_ptr;
-  bp.csr_idx = p->d_csr_idx;
-  bp.csc_ptr = p->d_csc_ptr;
-  bp.csc_idx = p->d_csc_idx;
+  bp.pair_ptr = p->d_pair_ptr;
+  bp.pair_idx = p->d_pair_idx;
+  bp.kpair_ptr = p->d_kpair_ptr;
+  bp.kpair_idx = p->d_kpair_idx;
   bp.q_stride = q_stride;
   bp.kv_stride = kv_stride;
   bp.nq = (int32_t)h.nq;
@@ -402,6 +410,8 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.heads = h.heads;
   bp.nqt = (int32_t)h.nqt;
   bp.nkt = (int32_t)h.nkt;
+  bp.n_pairs = (int32_t)h.n_pairs;
+  bp.n_kpairs = (int32_t)h.n_kpairs;
   bp.scale = scale;
   bp.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = nomas::launch_attn_bwd(bp, static_cast<hipStream_t>(hip_stream));

@@ -1,6 +1,475 @@
-// Backward kernels (placeholder until the gradient kernels land).
-#include "kernels.h"
+// Backward kernels of action-aware causal attention for gfx950 (CDNA4).
+//
+// Gradients of O = softmax(scale Q K^T + M) V (M = -inf on pairs the
+// segment-causal / action-window mask hides; "Model Architecture",
+// Segment-wise and Action-Aware Causal Attention) for an upstream dO, with P
+// recomputed from the forward's log-sum-exp:
+//   P = exp(scale S - lse),  dV = P^T dO,  dP = dO V^T,
+//   delta = rowsum(dO * O),  dS = P * (dP - delta),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Three launches on one stream:
+//   1. bwd_rowstats_kernel: delta and lse * log2(e) per (head, query);
+//   2. bwd_dkdv_kernel: one workgroup per pair of 64-key tiles of a head
+//      (four waves, 32 keys each, one wave per SIMD), looping over the
+//      q-tiles that see those keys (the union of the two key tiles' column
+//      lists); 128-query tiles of Q, dO and the row statistics are staged in
+//      LDS, double buffered; dK and dV accumulate in registers;
+//   3. bwd_dq_kernel: one workgroup per pair of 128-query tiles (eight waves,
+//      32 queries each) looping over the forward's key-tile lists, with K / V
+//      tiles staged as in the forward; dQ accumulates in registers.
+// Only FULL / PARTIAL tiles are visited and the per-element mask is applied on
+// PARTIAL (or ragged) tiles only, as in the forward.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   dK/dV wave (32 keys), per 32-query block b of a q-tile:
+//     S  (32 q x 32 k) = Q_b K^T     A: Q rows from LDS, B: K in registers
+//     dP (32 q x 32 k) = dO_b V^T    A: dO rows from LDS, B: V in registers
+//     dV^T (128 x 32 k) += dO_b^T P  A: dO^T (LDS transpose read), B: P
+//     dK^T (128 x 32 k) += Q_b^T dS  A: Q^T (LDS transpose read), B: dS
+//   The query rows of the first two products are permuted (kmap) so that P
+//   and dS come out of the accumulators already in B-operand order.
+//   dQ wave (32 queries), per 64-key tile:
+//     S^T = K Q^T, dP^T = V dO^T     A: K / V rows from LDS, B: Q / dO regs
+//     dQ^T (128 x 32 q) += K^T dS^T  A: K^T (LDS transpose read), B: dS^T
+// Both reuse the forward's swizzled LDS tile layout (tile_common.h); the
+// 128-row Q / dO tiles of the dK/dV kernel use the same layout with R = 128.
+#include "tile_common.h"
 
 namespace nomas {
-hipError_t launch_attn_bwd(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// 1. row statistics
+// ---------------------------------------------------------------------------
+
+// 16 lanes per (head, query row) over rows 0 .. nqt * 128 - 1; rows past nq
+// (and rows that see no key, lse = -inf) get delta = 0 and lse2 = 0: they are
+// masked wherever they occur, so only finiteness matters there.
+__global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
+  const int64_t rows = (int64_t)p.nqt * 128;
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (item >= rows * p.heads) return;  // whole 16-lane groups leave together
+  const int h = (int)(item / rows);
+  const int i = (int)(item - (int64_t)h * rows);
+  float acc = 0.f;
+  if (i < p.nq) {
+    const int64_t off = (int64_t)i * p.q_stride + (int64_t)h * D + 8 * sub;
+    const uint4 a = *reinterpret_cast<const uint4*>(p.o + off);
+    const uint4 b = *reinterpret_cast<const uint4*>(p.d_o + off);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc += __uint_as_float(av[j] << 16) * __uint_as_float(bv[j] << 16);
+      acc += __uint_as_float(av[j] & 0xffff0000u) * __uint_as_float(bv[j] & 0xffff0000u);
+    }
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (sub == 0) {
+    p.delta[item] = acc;
+    const float l = i < p.nq ? p.lse[(int64_t)h * p.nq + i] : -INFINITY;
+    p.lse2[item] = l == -INFINITY ? 0.f : l * LOG2E;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV
+// ---------------------------------------------------------------------------
+
+constexpr int KV_WAVES = 4;
+constexpr int KV_THREADS = 64 * KV_WAVES;
+constexpr int QT_ROWS = 128;
+constexpr int QTILE_BYTES = QT_ROWS * D * 2;         // 32 KB: a 128-row Q or dO tile
+constexpr int GRP128 = QT_ROWS * 64;                 // chunk-group stride of such a tile
+constexpr int STAT_OFF = 2 * QTILE_BYTES;            // lse2[128] | delta[128]
+constexpr int QD_OFF = STAT_OFF + 2 * QT_ROWS * 4;   // qdesc[128]
+constexpr int KV_STAGE_BYTES = QD_OFF + QT_ROWS * 16;
+
+// Stage q-tile qt of head h: Q and dO rows (rows past nq read row nq - 1:
+// masked), lse2 / delta, query descriptors.  Wave w fills row groups 2 w and
+// 2 w + 1 of both tiles (8 + 8 loads); wave 0 also the statistics, wave 1 the
+// descriptors.
+__device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt, char* stg,
+                                               int w, int lane) {
+  const int r_in = lane >> 2;
+  const int cl = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rg = 2 * w + j;
+    int row = qt * QT_ROWS + 16 * rg + r_in;
+    row = row < p.nq ? row : p.nq - 1;
+    const int64_t off = (int64_t)row * p.q_stride + (int64_t)h * D + 8 * cl;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      dma16(p.q + off + 32 * cg, stg + cg * GRP128 + rg * 1024);
+      dma16(p.d_o + off + 32 * cg, stg + QTILE_BYTES + cg * GRP128 + rg * 1024);
+    }
+  }
+  const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + (int64_t)qt * QT_ROWS;
+  if (w == 0) {
+    const float* src = lane < 32 ? p.lse2 + srow + 4 * lane : p.delta + srow + 4 * (lane - 32);
+    dma16(src, stg + STAT_OFF);
+  } else if (w == 1) {
+    const QDescDev* src = p.qdesc + (int64_t)qt * QT_ROWS + lane;
+    dma16(src, stg + QD_OFF);
+    dma16(src + 64, stg + QD_OFF + 1024);
+  }
+}
+
+struct KvWave {
+  bf16x8 kf[8];   // K row of this lane's key, dims [16 s + 8 hh, +8)
+  bf16x8 vf[8];   // V row, same layout
+  f32x16 dv[4];   // dV^T, dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
+  f32x16 dk[4];   // dK^T (unscaled)
+  int kseg;
+  uint32_t kbits;
+  int rbase[2];   // row-read base (Q / dO rows) for even / odd 16-dim steps
+  int tbase[2];   // transpose-read base for rows +0 / +4
+};
+
+// One staged q-tile against this wave's 32 keys.
+template <bool MASKED>
+__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, float scale_log2, int hh) {
+  const char* qtile = stg;
+  const char* dotile = stg + QTILE_BYTES;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int off = st.rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qtile + off);
+      const bf16x8 ado = *reinterpret_cast<const bf16x8*>(dotile + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, st.kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, st.vf[ks], dp, 0, 0, 0);
+    }
+    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8
+    float l2[16], dl[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+      const float4 lv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
+      const float4 dv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
+      l2[4 * g + 0] = lv.x; l2[4 * g + 1] = lv.y; l2[4 * g + 2] = lv.z; l2[4 * g + 3] = lv.w;
+      dl[4 * g + 0] = dv.x; dl[4 * g + 1] = dv.y; dl[4 * g + 2] = dv.z; dl[4 * g + 3] = dv.w;
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -l2[i]));
+      if (MASKED) {
+        const int ql = 32 * b + 16 * (i >> 3) + 8 * hh + (i & 7);
+        const QDescDev qd = *reinterpret_cast<const QDescDev*>(stg + QD_OFF + 16 * ql);
+        pv = visible(qd, st.kseg, st.kbits) ? pv : 0.f;
+      }
+      const float dsv = pv * (dp[i] - dl[i]);
+      pb[i >> 3][i & 7] = (__bf16)pv;
+      dsb[i >> 3][i & 7] = (__bf16)dsv;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int off = GRP128 * db + 1024 * (2 * b + half);
+        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + st.tbase[0]));
+        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + st.tbase[1]));
+        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + st.tbase[0]));
+        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + st.tbase[1]));
+        const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+        st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[half], st.dv[db], 0, 0, 0);
+        st.dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, dsb[half], st.dk[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Column of this lane's key: dims 32 db + 8 g + 4 hh + {0..3}.
+__device__ __forceinline__ void kv_store(uint16_t* dst, const f32x16* acc, float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(acc[db][4 * g + 0] * mul) | ((uint32_t)f2bf(acc[db][4 * g + 1] * mul) << 16);
+      pk.y = (uint32_t)f2bf(acc[db][4 * g + 2] * mul) | ((uint32_t)f2bf(acc[db][4 * g + 3] * mul) << 16);
+      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g + 4 * hh) = pk;
+    }
+}
+
+__global__ __launch_bounds__(KV_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char stg0[KV_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stg1[KV_STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jq = lane & 31, hh = lane >> 5;
+  const int unit = blockIdx.x;                 // h * n_kpairs + u
+  const int h = unit / p.n_kpairs;
+  const int u = unit - h * p.n_kpairs;
+  const int sub = w >> 1;                      // which key tile of the pair
+  const int key = (2 * u + sub) * BK + 32 * (w & 1) + jq;
+  const float scale_log2 = p.scale_log2;
+
+  KvWave st;
+  {
+    const int kr = key < p.nk ? key : p.nk - 1;  // rows past nk: computed, never stored
+    const uint16_t* ks = p.k + (int64_t)kr * p.kv_stride + (int64_t)h * D + 8 * hh;
+    const uint16_t* vs = p.v + (int64_t)kr * p.kv_stride + (int64_t)h * D + 8 * hh;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      st.kf[s8] = *reinterpret_cast<const bf16x8*>(ks + 16 * s8);
+      st.vf[s8] = *reinterpret_cast<const bf16x8*>(vs + 16 * s8);
+    }
+    // the second key tile of the last pair may not exist (its entries are
+    // all EMPTY for these waves)
+    const KDescDev kd = 2 * u + sub < p.nkt ? p.kdesc[(2 * u + sub) * BK + 32 * (w & 1) + jq]
+                                            : KDescDev{-1, 0u};
+    st.kseg = kd.seg;
+    st.kbits = kd.bits;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      st.dv[db] = f32x16{};
+      st.dk[db] = f32x16{};
+    }
+    const int rrow = kmap(jq), rsw = (rrow >> 2) & 3;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) st.rbase[e] = rrow * 64 + 16 * ((2 * e + hh) ^ rsw);
+    const int tr_j = (lane & 15) >> 2, tr_c4 = lane & 3;
+    const int x = 2 * ((lane >> 4) & 1) + (tr_c4 >> 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      st.tbase[r] = (8 * hh + tr_j + 4 * r) * 64 + 16 * (x ^ (2 * hh + r)) + 8 * (tr_c4 & 1);
+  }
+
+  const const_i32p ent = (const_i32p)p.kpair_idx + ((const_i32p)p.kpair_ptr)[u];
+  const int n_ent = ((const_i32p)p.kpair_ptr)[u + 1] - ((const_i32p)p.kpair_ptr)[u];
+  wait_vm_all();  // K / V rows in registers before the stage loads start
+
+  auto compute = [&](int t, const char* stg) {
+    const int e = ent[t];
+    if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
+    if ((e >> sub) & 1) kv_qtile<true>(st, stg, scale_log2, hh);
+    else kv_qtile<false>(st, stg, scale_log2, hh);
+  };
+  if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
+  for (int t = 0; t < n_ent; t += 2) {
+    wait_vm_all();   // this wave's loads of tile t
+    lds_barrier();   // everyone's; tile t - 1 (other stage) fully consumed
+    if (t + 1 < n_ent) kv_issue_stage(p, h, ent[t + 1] >> 4, stg1, w, lane);
+    compute(t, stg0);
+    if (t + 1 < n_ent) {
+      wait_vm_all();
+      lds_barrier();
+      if (t + 2 < n_ent) kv_issue_stage(p, h, ent[t + 2] >> 4, stg0, w, lane);
+      compute(t + 1, stg1);
+    }
+  }
+
+  if (key < p.nk) {
+    const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * D;
+    kv_store(p.dv + off, st.dv, 1.f, hh);
+    kv_store(p.dk + off, st.dk, p.scale, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ
+// ---------------------------------------------------------------------------
+
+constexpr int Q_WAVES = 8;
+constexpr int Q_THREADS = 64 * Q_WAVES;
+constexpr int Q_STAGE_BYTES = 2 * TILE_BYTES;  // K | V of one 64-key tile
+
+struct QWave {
+  bf16x8 qf[8];    // Q row of this lane's query, dims [16 s + 8 hh, +8)
+  bf16x8 dof[8];   // dO row, same layout
+  f32x16 acc[4];   // dQ^T (unscaled), dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
+  float lse2, delta;
+  QDescDev qd;
+  int kbase[2];    // K / V row-read base for even / odd 16-dim steps
+  int tbase[2];    // K transpose-read base for rows +0 / +4
+};
+
+template <bool MASKED>
+__device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile,
+                                        const KDescDev* kd, float scale_log2, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int off = st.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1);
+      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(ktile + off);
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vtile + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, st.qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, st.dof[ks], dp, 0, 0, 0);
+    }
+    // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int ri = 0; ri < 16; ++ri) {
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, -st.lse2));
+      if (MASKED) {
+        const KDescDev d = kd[32 * kb + 16 * (ri >> 3) + 8 * hh + (ri & 7)];
+        pv = visible(st.qd, d.seg, d.bits) ? pv : 0.f;
+      }
+      dsb[ri >> 3][ri & 7] = (__bf16)(pv * (dp[ri] - st.delta));
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const char* a = ktile + 4096 * db + 1024 * (2 * kb + half);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[1]));
+        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb[half], st.acc[db], 0, 0, 0);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char sbuf0[Q_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbuf1[Q_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbuf2[Q_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sbuf3[Q_STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) KDescDev skd0[BK];
+  __shared__ __attribute__((aligned(16))) KDescDev skd1[BK];
+  __shared__ __attribute__((aligned(16))) KDescDev skd2[BK];
+  __shared__ __attribute__((aligned(16))) KDescDev skd3[BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jq = lane & 31, hh = lane >> 5;
+  const int half = w >> 2;  // which q-tile of the pair
+  const int unit = blockIdx.x;
+  const int h = unit / p.n_pairs;
+  const int pr = unit - h * p.n_pairs;
+  const int qrow = pr * 256 + w * 32 + jq;
+  const float scale_log2 = p.scale_log2;
+
+  QWave st;
+  {
+    const int qr = qrow < p.nq ? qrow : p.nq - 1;  // rows past nq: computed, never stored
+    const int64_t off = (int64_t)qr * p.q_stride + (int64_t)h * D + 8 * hh;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      st.qf[s8] = *reinterpret_cast<const bf16x8*>(p.q + off + 16 * s8);
+      st.dof[s8] = *reinterpret_cast<const bf16x8*>(p.d_o + off + 16 * s8);
+    }
+    const bool in_tiles = qrow < p.nqt * QT_ROWS;
+    const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qrow;
+    st.lse2 = in_tiles ? p.lse2[srow] : 0.f;
+    st.delta = in_tiles ? p.delta[srow] : 0.f;
+    st.qd = in_tiles ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
+    const int krow = kmap(jq), ksw = (krow >> 2) & 3;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) st.kbase[e] = krow * 64 + 16 * ((2 * e + hh) ^ ksw);
+    const int tr_j = (lane & 15) >> 2, tr_c4 = lane & 3;
+    const int x = 2 * ((lane >> 4) & 1) + (tr_c4 >> 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      st.tbase[r] = (8 * hh + tr_j + 4 * r) * 64 + 16 * (x ^ (2 * hh + r)) + 8 * (tr_c4 & 1);
+  }
+
+  LoadCtx lc;
+  lc.kv_stride = p.kv_stride;
+  lc.nk = p.nk;
+  lc.n_cached = 0;
+  lc.lane_row = 16 * (w & 3) + (lane >> 2);
+  lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  lc.lane_cache = lc.lane_row * D + 8 * lc.lane_chunk;
+  lc.lane_new = (int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk;
+  lc.k_cache_h = p.k + (int64_t)h * D;  // unused: no cached keys
+  lc.v_cache_h = p.v + (int64_t)h * D;
+  lc.k_new_h = p.k + (int64_t)h * D;
+  lc.v_new_h = p.v + (int64_t)h * D;
+
+  const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
+  const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
+  wait_vm_all();  // rows and statistics in registers before the tile loads start
+
+  auto issue_tile = [&](int e, char* buf, KDescDev* kd) {
+    const int kt = ent[e] >> 4;
+    issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
+    issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
+    if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
+  };
+  auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) {
+    const int here = ent[t];
+    if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
+    if ((here >> half) & 1) dq_tile<true>(st, cbuf, cbuf + TILE_BYTES, ckd, scale_log2, hh);
+    else dq_tile<false>(st, cbuf, cbuf + TILE_BYTES, ckd, scale_log2, hh);
+  };
+  // four stages used as two pairs, one barrier per pair (as in the forward)
+  auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
+                  char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {
+    wait_vm_all();
+    lds_barrier();
+    if (t + 2 < n_ent) issue_tile(t + 2, n0, nk0);
+    if (t + 3 < n_ent) issue_tile(t + 3, n1, nk1);
+    tile(t, b0, k0);
+    if (t + 1 < n_ent) tile(t + 1, b1, k1);
+  };
+  if (n_ent > 0) issue_tile(0, sbuf0, skd0);
+  if (n_ent > 1) issue_tile(1, sbuf1, skd1);
+  for (int t = 0; t < n_ent; t += 4) {
+    pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
+    if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, sbuf0, skd0, sbuf1, skd1);
+  }
+
+  if (qrow < p.nq) {
+    uint16_t* dst = p.dq + (int64_t)qrow * p.q_stride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(st.acc[db][4 * g + 0] * p.scale) |
+               ((uint32_t)f2bf(st.acc[db][4 * g + 1] * p.scale) << 16);
+        pk.y = (uint32_t)f2bf(st.acc[db][4 * g + 2] * p.scale) |
+               ((uint32_t)f2bf(st.acc[db][4 * g + 3] * p.scale) << 16);
+        *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g + 4 * hh) = pk;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.heads <= 0) return hipSuccess;
+  const int64_t items = (int64_t)p.heads * p.nqt * QT_ROWS * 16;
+  if (items > 0) {
+    hipLaunchKernelGGL(bwd_rowstats_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nk > 0 && p.n_kpairs > 0) {
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.heads * p.n_kpairs)), dim3(KV_THREADS),
+                       0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.nq > 0 && p.n_pairs > 0) {
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.heads * p.n_pairs)), dim3(Q_THREADS), 0,
+                       stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace nomas

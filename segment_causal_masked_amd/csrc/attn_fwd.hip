@@ -40,120 +40,21 @@
 // changes rounding only; the half-wave exchange of the tile max is only needed
 // on that rare path.
 //
-// LDS tile layout (K and V alike, 64 rows x 16 chunks of 16 bytes): chunk c of
-// row r sits at (c / 4) * 4096 + r * 64 + 16 * ((c % 4) ^ ((r / 4) % 4)).
-// Each 16-lane phase of the K reads (16 rows, one chunk) and each 32-lane
-// phase of the V transpose reads (4 rows x 4 chunks x 8 bytes) covers all 64
-// banks exactly once, and every per-step address is an immediate offset from
-// two per-lane bases.  A 1 KB block (16 rows x one 4-chunk group) is filled
-// by a single direct HBM -> LDS load (global_load_lds_dwordx4).
-#include "kernels.h"
+// LDS tiles use the swizzled layout of tile_common.h (64 rows per K or V tile).
+#include "tile_common.h"
 
 namespace nomas {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef const __attribute__((address_space(4))) int32_t* const_i32p;
-typedef __attribute__((address_space(3))) i16x4* lds_i16x4p;
-
-constexpr int D = 128;
-constexpr int BK = 64;
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int UNIT_ROWS = 32 * NWAVES;  // 256 queries: a pair of 128-query tiles
 constexpr int NSTAGE = 4;
 constexpr int LOADS_PER_TILE = 4;       // per wave: 2 K + 2 V blocks (wave 0: + descriptors)
-constexpr int TILE_BYTES = BK * D * 2;  // 16 KB: one K or V tile
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 constexpr float RESCALE_SLACK = 8.0f;
 // per partial piece: for each thread, 64 O values + max + sum
 constexpr int SLOT_FLOATS = NTHREADS * 66;
-
-// MFMA output row i (of 32) -> key offset inside a 32-key block.
-__device__ __forceinline__ int kmap(int i) {
-  const int g = i >> 3, q = (i >> 2) & 1, r = i & 3;
-  return 16 * (g >> 1) + 8 * q + 4 * (g & 1) + r;
-}
-
-// Branch-free (bitwise, not short-circuit), so that masking compiles to
-// compares and selects on the score registers in place.
-__device__ __forceinline__ bool visible(const QDescDev& q, int kseg, uint32_t kbits) {
-  const bool in_range = (kseg >= q.lo) & (kseg <= q.seg);
-  const bool tail_ok = (kseg == q.seg) & ((q.amask & kbits) != 0u);
-  return in_range & ((kbits == 0u) | tail_ok);
-}
-
-__device__ __forceinline__ uint16_t f2bf(float x) {
-  __bf16 b = (__bf16)x;  // round to nearest even
-  return __builtin_bit_cast(uint16_t, b);
-}
-
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// 16-byte direct load HBM -> LDS (global_load_lds_dwordx4): lane i's 16 bytes
-// land at lds + 16 * i.  Issued through inline asm so that the compiler does
-// not track it: its alias analysis for in-flight LDS DMA is conservative and
-// would drain every prefetch at the next LDS read or fence.  The instruction
-// writes no VGPR (only LDS), so nothing the compiler sees can be overwritten
-// late; completion of a stage is ensured explicitly with s_waitcnt vmcnt
-// before the barrier that publishes it.  Waits the compiler inserts for its
-// own loads stay correct (only stricter): vector memory ops complete in order.
-__device__ __forceinline__ void dma16(const void* gsrc, const void* lds_dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)((const __attribute__((address_space(3))) char*)lds_dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
-}
-
-// Workgroup barrier ordering LDS accesses only (no wait on global memory).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// s_waitcnt vmcnt(N) (expcnt, lgkmcnt untouched): N in [0, 63].
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Everything the tile loads need, copied out of the kernel arguments.
-// Wave w fills LDS blocks (chunk group w / 4 + 2 i, rows 16 (w % 4) ..+15) of
-// a tile for i = 0, 1.  Lane l fetches row 16 (w % 4) + l / 4 and chunk
-// 4 (w / 4 + 2 i) + ((l % 4) ^ ((l / 16) % 4)): its offset inside a tile is
-// constant up to the scalar 32 (w / 4 + 2 i).
-struct LoadCtx {
-  const uint16_t *k_cache_h, *v_cache_h;  // head h's rows in the cache
-  const uint16_t *k_new_h, *v_new_h;      // head h's column in the new-token rows
-  int64_t kv_stride;                      // new-token stride (elements)
-  int32_t nk, n_cached;
-  int32_t lane_row, lane_chunk;           // this lane's row / chunk inside a block
-  int32_t lane_cache, lane_new;           // element offsets of (lane_row, lane_chunk)
-};
-
-__device__ __forceinline__ void issue_half(const LoadCtx& c, const uint16_t* cache_h,
-                                           const uint16_t* new_h, char* dst, int kt, int w) {
-  const int k0 = kt * BK;
-  const int gq = w >> 2;
-  char* d = dst + 4096 * gq + 1024 * (w & 3);
-  const uint16_t* src;
-  if (k0 + BK <= c.n_cached) {
-    src = cache_h + (int64_t)k0 * D + c.lane_cache;
-  } else if (k0 >= c.n_cached && k0 + BK <= c.nk) {
-    src = new_h + (int64_t)(k0 - c.n_cached) * c.kv_stride + c.lane_new;
-  } else {  // straddles the cache / new boundary or runs past the last key
-    int key = k0 + c.lane_row;
-    key = key < c.nk ? key : c.nk - 1;  // any valid row: masked later
-    src = (key < c.n_cached ? cache_h + (int64_t)key * D
-                            : new_h + (int64_t)(key - c.n_cached) * c.kv_stride) + 8 * c.lane_chunk;
-  }
-  src += 32 * gq;
-  dma16(src, d);
-  dma16(src + 64, d + 8192);
-}
 
 struct WaveState {
   bf16x8 qf[8];     // Q fragment: query jq, dims [16 s + 8 hh, +8)

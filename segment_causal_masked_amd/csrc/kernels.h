@@ -54,15 +54,17 @@ struct AppendParams {
 hipError_t launch_kvcache_append(const AppendParams& p, hipStream_t stream);
 
 struct BwdParams {
-  const uint16_t *q, *k, *v, *o, *d_o;
-  const float* lse;        // [H][nq]
-  uint16_t *dq, *dk, *dv;
-  float* delta;            // workspace [H][nqt*128]
-  const QDescDev* qdesc;
-  const KDescDev* kdesc;
-  const int32_t *csr_ptr, *csr_idx, *csc_ptr, *csc_idx;
+  const uint16_t *q, *k, *v, *o, *d_o;  // [T][H][128] bf16 (q, o, d_o: q_stride; k, v: kv_stride)
+  const float* lse;        // [H][nq], natural log (from the forward)
+  uint16_t *dq, *dk, *dv;  // outputs, same layouts as q / k / v
+  float* delta;            // workspace [H][nqt*128]: rowsum(dO * O)
+  float* lse2;             // workspace [H][nqt*128]: lse * log2(e), 0 where -inf or padding
+  const QDescDev* qdesc;   // nqt*128 entries
+  const KDescDev* kdesc;   // nkt*64 entries
+  const int32_t *pair_ptr, *pair_idx;    // per q-tile pair: the forward's key-tile lists
+  const int32_t *kpair_ptr, *kpair_idx;  // per key-tile pair: (q_tile << 4) | flags
   int64_t q_stride, kv_stride;
-  int32_t nq, nk, heads, nqt, nkt;
+  int32_t nq, nk, heads, nqt, nkt, n_pairs, n_kpairs;
   float scale, scale_log2;
 };
 

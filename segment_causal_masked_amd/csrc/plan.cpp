@@ -360,4 +360,32 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   }
 }
 
+void build_bwd_schedule(HostPlan* pp) {
+  HostPlan& p = *pp;
+  // merged CSC lists of k-tile pairs (2 u, 2 u + 1); a ragged last q-tile is
+  // masked too, since its rows past the end must not reach dK / dV
+  const bool ragged_q = p.nq % p.bq != 0;
+  p.n_kpairs = (p.nkt + 1) / 2;
+  p.kpair_ptr.assign(size_t(p.n_kpairs + 1), 0);
+  p.kpair_idx.clear();
+  for (int64_t u = 0; u < p.n_kpairs; ++u) {
+    const int64_t ka = 2 * u, kb = 2 * u + 1;
+    int32_t ia = p.csc_ptr[size_t(ka)], ea = p.csc_ptr[size_t(ka + 1)];
+    int32_t ib = kb < p.nkt ? p.csc_ptr[size_t(kb)] : 0, eb = kb < p.nkt ? p.csc_ptr[size_t(kb + 1)] : 0;
+    while (ia < ea || ib < eb) {
+      const int32_t qa = ia < ea ? (p.csc_idx[size_t(ia)] >> 1) : INT32_MAX;
+      const int32_t qb = ib < eb ? (p.csc_idx[size_t(ib)] >> 1) : INT32_MAX;
+      const int32_t qt = std::min(qa, qb);
+      const int32_t rq = (ragged_q && qt == p.nqt - 1) ? 1 : 0;
+      int32_t flags = 0;
+      if (qa == qt) flags |= (p.csc_idx[size_t(ia++)] & 1) | rq;
+      else flags |= 4;  // EMPTY for the first k-tile
+      if (qb == qt) flags |= ((p.csc_idx[size_t(ib++)] & 1) | rq) << 1;
+      else flags |= 8;  // EMPTY for the second k-tile (or it does not exist)
+      p.kpair_idx.push_back((qt << 4) | flags);
+    }
+    p.kpair_ptr[size_t(u + 1)] = int32_t(p.kpair_idx.size());
+  }
+}
+
 }  // namespace nomas

@@ -41,9 +41,10 @@ inline bool visible(const QDesc& q, const KDesc& k) {
 // entries are the union of the two q-tiles' non-empty key tiles, each entry
 // = (k_tile << 4) | flags: bit 0 / 1 = the first / second q-tile needs the
 // per-element mask there, bit 2 / 3 = the tile is EMPTY for the first /
-// second q-tile (its waves skip it).  The iterations (unit, entry)  They are cut into `groups` contiguous,
-// equal ranges, one per persistent workgroup; a unit cut by a range boundary
-// becomes several pieces whose partial results are merged afterwards.
+// second q-tile (its waves skip it).  The (unit, entry) iterations are cut
+// into `groups` contiguous, equal ranges, one per persistent workgroup; a unit
+// cut by a range boundary becomes several pieces whose partial results are
+// merged afterwards.
 struct Piece {
   int32_t unit, e_begin, e_end, slot;  // slot = partial-result slot, -1 = final
 };
@@ -72,10 +73,19 @@ struct HostPlan {
   std::vector<Piece> pieces;
   std::vector<CombineItem> combine;
   int32_t n_slots = 0;
+  // backward schedule (build_bwd_schedule): per pair of key tiles (2 u,
+  // 2 u + 1) the union of their non-empty q-tiles, entry = (q_tile << 4) |
+  // flags with bit 0 / 1 = mask for the first / second key tile (PARTIAL,
+  // ragged key tile or ragged last q-tile), bit 2 / 3 = EMPTY for it
+  int64_t n_kpairs = 0;
+  std::vector<int32_t> kpair_ptr, kpair_idx;
 };
 
 // Cut the forward iterations into `groups` equal contiguous ranges.
 void build_fwd_schedule(HostPlan* p, int32_t groups);
+
+// Merged per-key-tile-pair lists for the dK / dV kernel.
+void build_bwd_schedule(HostPlan* p);
 
 // Identity of a cache's committed segments (used for stale-plan checks).
 struct CacheState {
