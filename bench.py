@@ -16,6 +16,9 @@ kernel that merges split query tiles, back to back on one stream): the same
 effective FLOPs per call / the call's average duration (HIP events on the
 launch stream), against the bf16 dense MFMA peak of MI355X.
 cpu_baseline = the fp64 oracle on one forward call of the same workload.
+training_pack (extra, not the headline) = forward and backward times on the
+131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
+(four products) and, beside it, the FlashAttention convention 10 D H A.
 """
 from __future__ import annotations
 
@@ -96,6 +99,49 @@ def cpu_baseline(w):
             "cpu": cpu_model()}
 
 
+def bench_training(nm, wl, torch, iters=5, warmup=2):
+    """Forward + backward on the 131072-token training pack (4 videos, 16 heads):
+    mean time of each over `iters` calls after `warmup`, HIP events on the
+    launch stream.  Inputs are drawn on the device (timing only)."""
+    w = wl.config5()
+    H, D = w.heads, 128
+    t0 = time.perf_counter()
+    plan = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=H)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info()
+    A = info.unmasked_pairs
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000)
+    mk = lambda: torch.randn((w.n_q, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    q, k, v, d_o = mk(), mk(), mk(), mk()
+    o = torch.empty_like(q)
+    lse = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fws = torch.empty(max(nm.nomas_attn_fwd_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(max(nm.nomas_attn_bwd_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fwd_ms, bwd_ms = [], []
+    for it in range(warmup + iters):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        nm.nomas_attn_fwd(plan, None, q, k, v, o, lse, D ** -0.5, workspace=fws)
+        e[1].record(stream)
+        nm.nomas_attn_bwd(plan, q, k, v, o, d_o, lse, dq, dk, dv, D ** -0.5, workspace=bws)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if it >= warmup:
+            fwd_ms.append(e[0].elapsed_time(e[1]))
+            bwd_ms.append(e[1].elapsed_time(e[2]))
+    f, b = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+    return {"workload": w.name, "tokens": w.n_q, "heads": H, "unmasked_pairs": A,
+            "plan_host_ms": round(plan_ms, 2),
+            "fwd_ms": round(f, 3), "fwd_tflops": round(4.0 * D * H * A / (f * 1e-3) / 1e12, 2),
+            "bwd_ms": round(b, 3),
+            "bwd_tflops_8DHA": round(8.0 * D * H * A / (b * 1e-3) / 1e12, 2),
+            "bwd_tflops_10DHA": round(10.0 * D * H * A / (b * 1e-3) / 1e12, 2),
+            "iters": iters}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the extra forward + backward row on the 131072-token pack")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (untimed), as a known "
                          "quantity for calibrating HBM byte counters")
@@ -246,6 +294,8 @@ def main():
         "plan_host_ms": round(plan_ms, 3),
         "kernel_sha": kernel_hash(),
     }
+    if not args.no_training:
+        line["training_pack"] = bench_training(nm, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

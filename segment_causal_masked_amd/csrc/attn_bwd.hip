@@ -253,7 +253,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int n_ent = ((const_i32p)p.kpair_ptr)[u + 1] - ((const_i32p)p.kpair_ptr)[u];
   wait_vm_all();  // K / V rows in registers before the stage loads start
 
-  auto compute = [&](int t, const char* stg) {
+  auto compute = [&](int t, const char* stg) __attribute__((always_inline)) {
     const int e = ent[t];
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
     if ((e >> sub) & 1) kv_qtile<true>(st, stg, scale_log2, hh);
@@ -298,41 +298,76 @@ struct QWave {
   int tbase[2];    // K transpose-read base for rows +0 / +4
 };
 
+// Visibility of this lane's query against the 32 keys it holds scores for in
+// a 64-key tile: bit 16 kb + ri <-> key 32 kb + 16 (ri / 8) + 8 hh + ri % 8.
+// Computed before the products, while few registers are live.
+__device__ __forceinline__ uint32_t dq_vis_bits(const QDescDev& qd, const KDescDev* kd, int hh) {
+  uint32_t v = 0;
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    const KDescDev d = kd[32 * (j >> 4) + 16 * ((j >> 3) & 1) + 8 * hh + (j & 7)];
+    v |= (uint32_t)visible(qd, d.seg, d.bits) << j;
+  }
+  return v;
+}
+
 template <bool MASKED>
 __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile,
-                                        const KDescDev* kd, float scale_log2, int hh) {
+                                        uint32_t vis, float scale_log2, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    // S^T and dP^T for keys 32 kb + (0..31): two chains, interleaved, with the
+    // K / V row fragments read two MFMA pairs ahead
     f32x16 s = f32x16{}, dp = f32x16{};
+    auto rd = [&](const char* t, int ks) {
+      return *reinterpret_cast<const bf16x8*>(t + st.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
+    };
+    bf16x8 fk[2], fv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fk[i] = rd(ktile, i);
+      fv[i] = rd(vtile, i);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int off = st.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1);
-      const bf16x8 ak = *reinterpret_cast<const bf16x8*>(ktile + off);
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vtile + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, st.qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, st.dof[ks], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[ks & 1], st.dof[ks], dp, 0, 0, 0);
+      if (ks + 2 < 8) {
+        fk[ks & 1] = rd(ktile, ks + 2);
+        fv[ks & 1] = rd(vtile, ks + 2);
+      }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
     // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
     bf16x8 dsb[2];
 #pragma unroll
     for (int ri = 0; ri < 16; ++ri) {
       float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, -st.lse2));
-      if (MASKED) {
-        const KDescDev d = kd[32 * kb + 16 * (ri >> 3) + 8 * hh + (ri & 7)];
-        pv = visible(st.qd, d.seg, d.bits) ? pv : 0.f;
-      }
+      if (MASKED) pv = ((vis >> (16 * kb + ri)) & 1u) ? pv : 0.f;
       dsb[ri >> 3][ri & 7] = (__bf16)(pv * (dp[ri] - st.delta));
     }
+
+    // dQ^T += K^T dS^T over the two 16-key steps of this half
+    auto tr = [&](int i) {  // i = 4 half + db
+      const char* a = ktile + 4096 * (i & 3) + 1024 * (2 * kb + (i >> 2));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[1]));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 ft[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int i = 0; i < 2; ++i) ft[i] = tr(i);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const char* a = ktile + 4096 * db + 1024 * (2 * kb + half);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(a + st.tbase[1]));
-        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsb[half], st.acc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < 8; ++i) {
+      st.acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ft[i & 1], dsb[i >> 2], st.acc[i & 3], 0, 0, 0);
+      if (i + 2 < 8) ft[i & 1] = tr(i + 2);
     }
   }
 }
@@ -401,21 +436,24 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
   wait_vm_all();  // rows and statistics in registers before the tile loads start
 
-  auto issue_tile = [&](int e, char* buf, KDescDev* kd) {
+  // (always_inline: otherwise the wave state would be passed through scratch)
+  auto issue_tile = [&](int e, char* buf, KDescDev* kd) __attribute__((always_inline)) {
     const int kt = ent[e] >> 4;
     issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
     issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
     if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
   };
-  auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) {
+  auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
     const int here = ent[t];
     if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
-    if ((here >> half) & 1) dq_tile<true>(st, cbuf, cbuf + TILE_BYTES, ckd, scale_log2, hh);
-    else dq_tile<false>(st, cbuf, cbuf + TILE_BYTES, ckd, scale_log2, hh);
+    // one code path for FULL and PARTIAL tiles (a second variant would push
+    // the wave past its 256 registers): FULL tiles select with all bits set
+    const uint32_t vis = ((here >> half) & 1) ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
+    dq_tile<true>(st, cbuf, cbuf + TILE_BYTES, vis, scale_log2, hh);
   };
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
-                  char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {
+                  char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) __attribute__((always_inline)) {
     wait_vm_all();
     lds_barrier();
     if (t + 2 < n_ent) issue_tile(t + 2, n0, nk0);
