@@ -70,33 +70,39 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w):
+def cpu_baseline(w, runs=3):
     """The fp64 oracle (numpy, BLAS threads = this process's cores) on one full
-    forward call of the same workload: all 16 heads, every query of the new
-    segment against all cached + new keys."""
+    forward call of the same workload -- all 16 heads, every query of the new
+    segment against all cached + new keys -- median of `runs` runs."""
     import oracle
+    cores, blas = len(os.sched_getaffinity(0)), "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()
-                     if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            cores = max(i.get("num_threads", 1) for i in infos)
+            blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in infos}))
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        pass
     keys = w.cached + w.new
     kc, vc = w.cache_kv()
     q = w.q()
     k = np.concatenate([kc, w.k_new()])
     v = np.concatenate([vc, w.v_new()])
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
-    t0 = time.perf_counter()
-    oracle.forward(q, k, v, tq, tk, 128 ** -0.5)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, tq, tk, 128 ** -0.5)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     a = oracle.unmasked_pairs(tq, tk)
     flop = 4.0 * 128 * w.heads * a
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"one forward call of {w.name} ({w.heads} heads, {w.n_q} queries x "
-                      f"{w.n_keys} keys), fp64 numpy, single run: {dt:.1f} s",
-            "cpu": cpu_model()}
+                      f"{w.n_keys} keys), fp64 numpy, median of {runs} runs: {dt:.2f} s",
+            "cpu": cpu_model(), "blas": blas}
 
 
 def bench_training(nm, wl, torch, iters=5, warmup=2):
