@@ -16,6 +16,8 @@ kernel that merges split query tiles, back to back on one stream): the same
 effective FLOPs per call / the call's average duration (HIP events on the
 launch stream), against the bf16 dense MFMA peak of MI355X.
 cpu_baseline = the fp64 oracle on one forward call of the same workload.
+long_session (extra) = the 720p long session: 4 forward calls over 16 cached
+segments + the new one (122,944 keys), then the append.
 training_pack (extra, not the headline) = forward and backward times on the
 131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
 (four products) and, beside it, the FlashAttention convention 10 D H A.
@@ -148,6 +150,61 @@ def bench_training(nm, wl, torch, iters=5, warmup=2):
             "iters": iters}
 
 
+def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
+    """720p long session: 16 cached segments (7,232 tokens each) + the new
+    segment; per session 4 forward calls with fresh Q / K_new / V_new, then the
+    append of the new segment (rolled back after each session).  Inputs are
+    drawn on the device (timing only)."""
+    w = wl.config4()
+    H, D = w.heads, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4000)
+    rnd = lambda n: torch.randn((n, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    cap = w.n_cached + w.n_new
+    kb = torch.empty((H, cap, D), dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty_like(kb)
+    cache = nm.nomas_kvcache_create(H, cap, kb, vb)
+    for s in w.cached:
+        nm.nomas_kvcache_append(cache, s, rnd(s.n_tokens), rnd(s.n_tokens))
+    t0 = time.perf_counter()
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    A = plan.info().unmasked_pairs
+    qs = [rnd(w.n_q) for _ in range(4)]
+    ks = [rnd(w.n_new) for _ in range(4)]
+    vs = [rnd(w.n_new) for _ in range(4)]
+    o = torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(nm.nomas_attn_fwd_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call_ms, app_ms, sess_ms = [], [], []
+    n_seg = len(w.cached)
+    for it in range(warmup + sessions):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        for n in range(4):
+            nm.nomas_attn_fwd(plan, cache, qs[n], ks[n], vs[n], o, lse, D ** -0.5, workspace=ws)
+            ev[n + 1].record(stream)
+        nm.nomas_kvcache_append(cache, w.new[0], ks[3], vs[3])
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        nm.nomas_kvcache_truncate(cache, n_seg)
+        if it >= warmup:
+            call_ms += [ev[n].elapsed_time(ev[n + 1]) for n in range(4)]
+            app_ms.append(ev[4].elapsed_time(ev[5]))
+            sess_ms.append(ev[0].elapsed_time(ev[5]))
+    c, a = float(np.mean(call_ms)), float(np.mean(app_ms))
+    app_bytes = 2 * 2 * w.n_new * H * D * 2
+    kv_bytes = 2 * w.n_keys * H * D * 2
+    return {"workload": w.name, "queries": w.n_q, "keys": w.n_keys, "heads": H,
+            "unmasked_pairs": A, "plan_host_ms": round(plan_ms, 2),
+            "fwd_ms_per_call": round(c, 3),
+            "fwd_tflops": round(4.0 * D * H * A / (c * 1e-3) / 1e12, 2),
+            "kv_stream_gbs": round(kv_bytes / (c * 1e-3) / 1e9, 1),
+            "append_ms": round(a, 4), "append_gbs": round(app_bytes / (a * 1e-3) / 1e9, 1),
+            "session_ms": round(float(np.mean(sess_ms)), 3), "sessions": sessions}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +214,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the extra forward + backward row on the 131072-token pack")
+    ap.add_argument("--no-long-session", action="store_true",
+                    help="skip the extra 720p long-session row")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (untimed), as a known "
                          "quantity for calibrating HBM byte counters")
@@ -300,6 +359,8 @@ def main():
         "plan_host_ms": round(plan_ms, 3),
         "kernel_sha": kernel_hash(),
     }
+    if not args.no_long_session:
+        line["long_session"] = bench_long_session(nm, wl, torch)
     if not args.no_training:
         line["training_pack"] = bench_training(nm, wl, torch)
     if not args.no_cpu_baseline:
