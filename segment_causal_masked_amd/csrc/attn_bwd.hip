@@ -437,14 +437,12 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   wait_vm_all();  // rows and statistics in registers before the tile loads start
 
   // (always_inline: otherwise the wave state would be passed through scratch)
-  auto issue_tile = [&](int e, char* buf, KDescDev* kd) __attribute__((always_inline)) {
-    const int kt = ent[e] >> 4;
+  auto issue_tile = [&](int kt, char* buf, KDescDev* kd) __attribute__((always_inline)) {
     issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
     issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
     if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
   };
-  auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
-    const int here = ent[t];
+  auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
     if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
     // one code path for FULL and PARTIAL tiles (a second variant would push
     // the wave past its 256 registers): FULL tiles select with all bits set
@@ -454,15 +452,20 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
                   char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) __attribute__((always_inline)) {
+    const int last = n_ent - 1;
+    const int e0 = ent[t], e1 = ent[min(t + 1, last)];
+    int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
+    // (pin the loads here: otherwise they are rematerialised after the barrier)
+    asm volatile("" : "+s"(e2), "+s"(e3));
     wait_vm_all();
     lds_barrier();
-    if (t + 2 < n_ent) issue_tile(t + 2, n0, nk0);
-    if (t + 3 < n_ent) issue_tile(t + 3, n1, nk1);
-    tile(t, b0, k0);
-    if (t + 1 < n_ent) tile(t + 1, b1, k1);
+    if (t + 2 < n_ent) issue_tile(e2 >> 4, n0, nk0);
+    if (t + 3 < n_ent) issue_tile(e3 >> 4, n1, nk1);
+    tile(e0, b0, k0);
+    if (t + 1 < n_ent) tile(e1, b1, k1);
   };
-  if (n_ent > 0) issue_tile(0, sbuf0, skd0);
-  if (n_ent > 1) issue_tile(1, sbuf1, skd1);
+  if (n_ent > 0) issue_tile(ent[0] >> 4, sbuf0, skd0);
+  if (n_ent > 1) issue_tile(ent[1] >> 4, sbuf1, skd1);
   for (int t = 0; t < n_ent; t += 4) {
     pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
     if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, sbuf0, skd0, sbuf1, skd1);

@@ -290,31 +290,36 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // would also drain the tile prefetches issued below.
     wait_vm_all();
 
-    auto issue_tile = [&](int e, char* buf, KDescDev* kd) {
-      const int kt = ent[e] >> 4;
+    auto issue_tile = [&](int kt, char* buf, KDescDev* kd) {
       issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
       issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
       if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
     };
-    if (n_ent > 0) issue_tile(0, sbuf0, skd0);
-    if (n_ent > 1) issue_tile(1, sbuf1, skd1);
+    if (n_ent > 0) issue_tile(ent[0] >> 4, sbuf0, skd0);
+    if (n_ent > 1) issue_tile(ent[1] >> 4, sbuf1, skd1);
 
     // Tiles go in pairs: iteration j computes tiles 2j, 2j+1 (buffers of one
     // half of the ring) after issuing tiles 2j+2, 2j+3 into the other half,
     // which the barrier has just released; one barrier per two tiles.
-    auto tile = [&](int t, const char* cbuf, const KDescDev* ckd) {
-      const int here = ent[t];
+    auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) {
       if (!((here >> (2 + half)) & 1))  // not EMPTY for this wave's q-tile
         tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, (here >> half) & 1, scale_log2, hh);
     };
     auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
                     char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {
+      // the four entries this pair needs, read before the barrier (their
+      // scalar-load latency then overlaps the wait instead of following it)
+      const int last = n_ent - 1;
+      const int e0 = ent[t], e1 = ent[min(t + 1, last)];
+      int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
+      // (pin the loads here: otherwise they are rematerialised after the barrier)
+      asm volatile("" : "+s"(e2), "+s"(e3));
       wait_vm_all();  // this wave's loads of tiles t, t+1 (the only ones in flight)
       lds_barrier();  // ... and every other wave's; tiles t-2, t-1 fully consumed
-      if (t + 2 < n_ent) issue_tile(t + 2, n0, nk0);
-      if (t + 3 < n_ent) issue_tile(t + 3, n1, nk1);
-      tile(t, b0, k0);
-      if (t + 1 < n_ent) tile(t + 1, b1, k1);
+      if (t + 2 < n_ent) issue_tile(e2 >> 4, n0, nk0);
+      if (t + 3 < n_ent) issue_tile(e3 >> 4, n1, nk1);
+      tile(e0, b0, k0);
+      if (t + 1 < n_ent) tile(e1, b1, k1);
     };
     for (int t = 0; t < n_ent; t += 4) {
       pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
