@@ -33,12 +33,13 @@
 // registers.  V^T operands come straight from the V tile with the LDS
 // transpose read (ds_read_b64_tr_b16).
 //
-// The reference max is only raised when a row's tile max exceeds it by more
-// than RESCALE_SLACK (log2 units); until then exp2 arguments stay <=
-// RESCALE_SLACK, P <= 2^RESCALE_SLACK, and the O rescale (64 multiplies per
-// lane) is skipped.  O / l does not depend on the reference max, so this
-// changes rounding only; the half-wave exchange of the tile max is only needed
-// on that rare path.
+// The reference max is not recomputed per tile.  P is formed against the
+// row's current reference, which is set to an exact tile max; only when a
+// half-wave's sum of P exceeds RESCALE_SUM (a score far above the reference,
+// or a row that has not seen a visible key yet) does the wave take the exact
+// path: row max over the tile (half-wave exchange), O and the sum rescaled,
+// P formed again.  O / l does not depend on the reference, so this changes
+// rounding only, and P stays <= RESCALE_SUM, far from fp32 / bf16 limits.
 //
 // LDS tiles use the swizzled layout of tile_common.h (64 rows per K or V tile).
 #include "tile_common.h"
@@ -52,7 +53,9 @@ constexpr int UNIT_ROWS = 32 * NWAVES;  // 256 queries: a pair of 128-query tile
 constexpr int NSTAGE = 4;
 constexpr int LOADS_PER_TILE = 4;       // per wave: 2 K + 2 V blocks (wave 0: + descriptors)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-constexpr float RESCALE_SLACK = 8.0f;
+// A half-wave's sum of P over its 32 keys above this value sends the wave to
+// the exact path (new reference = the row max); below it every P <= 2^16.
+constexpr float RESCALE_SUM = 65536.0f;
 // per partial piece: for each thread, 64 O values + max + sum
 constexpr int SLOT_FLOATS = NTHREADS * 66;
 
@@ -120,52 +123,59 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
         s[kb][ri] = visible(ws.qd, d.seg, d.bits) ? s[kb][ri] : -INFINITY;
       }
   }
-  // this half-wave's max over its 32 keys: a 16-op max3 tree
-  float t[12];
+  // P = exp2(s * scale_log2 - m) in fp32 against the row's reference m,
+  // summed in fp32 (four chains) and rounded to bf16 as the P.V operand.
+  bf16x8 pf[4];  // P^T operand for step (kb, half) = 2 kb + half
+  float l_half;  // this half-wave's sum over its 32 keys
+  auto probs = [&](float m_use) {
+    float lsum[4];
 #pragma unroll
-  for (int j = 0; j < 5; ++j) t[j] = fmaxf(fmaxf(s[0][3 * j], s[0][3 * j + 1]), s[0][3 * j + 2]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-  for (int j = 0; j < 5; ++j) t[5 + j] = fmaxf(fmaxf(s[1][3 * j], s[1][3 * j + 1]), s[1][3 * j + 2]);
-  t[10] = s[0][15];
-  t[11] = s[1][15];
-  const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
-  const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(fmaxf(t[9], t[10]), t[11]);
-  const float mx = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
-  const float m_half = mx * scale_log2;
-  // Raise the reference max only when a row's tile max exceeds it by more than
-  // RESCALE_SLACK; the decision is per row (both halves agree after the
-  // exchange), the branch only skips work no row of the wave needs.
-  if (__builtin_amdgcn_ballot_w64(m_half > ws.m_run + RESCALE_SLACK)) {
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 v;
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const float pe = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s[kb][8 * half + e8], scale_log2, -m_use));
+          lsum[e8 & 3] = (kb | half | (e8 >> 2)) ? lsum[e8 & 3] + pe : pe;
+          v[e8] = (__bf16)pe;
+        }
+        pf[2 * kb + half] = v;
+      }
+    l_half = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+  };
+  // Common path: no max at all.  P is formed against the current reference
+  // (0 while the row has seen no visible key); a row needs a new reference
+  // only if it has none yet or a half's sum exceeds RESCALE_SUM (a score far
+  // above the reference, or an overflow).  Then the wave computes the row
+  // maxima, and each such row -- only those, so a row's result depends on its
+  // own scores alone -- takes max(reference, row max), rescales O and its sum
+  // and forms P again (rows keeping their reference recompute the same P).
+  probs(ws.m_run == -INFINITY ? 0.f : ws.m_run);
+  const bool need_half = ws.m_run == -INFINITY || !(l_half <= RESCALE_SUM);
+  if (__builtin_amdgcn_ballot_w64(need_half)) {
+    float t[12];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) t[j] = fmaxf(fmaxf(s[0][3 * j], s[0][3 * j + 1]), s[0][3 * j + 2]);
+#pragma unroll
+    for (int j = 0; j < 5; ++j) t[5 + j] = fmaxf(fmaxf(s[1][3 * j], s[1][3 * j + 1]), s[1][3 * j + 2]);
+    t[10] = s[0][15];
+    t[11] = s[1][15];
+    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+    const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(fmaxf(t[9], t[10]), t[11]);
+    const float m_half = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3) * scale_log2;
     const float m_row = fmaxf(m_half, __shfl_xor(m_half, 32));
-    const bool raise = m_row > ws.m_run + RESCALE_SLACK;
-    const float m_new = raise ? m_row : ws.m_run;
-    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - (m_new == -INFINITY ? 0.f : m_new));
+    const bool need_row = need_half || __shfl_xor((int)need_half, 32);
+    const float m_new = need_row ? fmaxf(ws.m_run, m_row) : ws.m_run;
+    const float alpha = m_new == ws.m_run ? 1.f : __builtin_amdgcn_exp2f(ws.m_run - m_new);
     ws.m_run = m_new;
     ws.l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < 4; ++db) ws.acc[db] *= alpha;
+    probs(m_new == -INFINITY ? 0.f : m_new);
   }
-  const float m_use = ws.m_run == -INFINITY ? 0.f : ws.m_run;
-
-  // P = exp2(s * scale_log2 - m) in fp32, summed in fp32 (four chains) and
-  // rounded to bf16 as the operand of the P.V product.
-  bf16x8 pf[4];  // P^T operand for step (kb, half) = 2 kb + half
-  float lsum[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      bf16x8 v;
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const float pe = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(s[kb][8 * half + e8], scale_log2, -m_use));
-        lsum[e8 & 3] = (kb | half | (e8 >> 2)) ? lsum[e8 & 3] + pe : pe;
-        v[e8] = (__bf16)pe;
-      }
-      pf[2 * kb + half] = v;
-    }
-  ws.l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+  ws.l_run += l_half;
 
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
