@@ -65,6 +65,7 @@ struct nomas_plan {
   const int4 *d_pieces = nullptr, *d_combine = nullptr;
   const int32_t *d_pair_ptr = nullptr, *d_pair_idx = nullptr;
   const int32_t *d_kpair_ptr = nullptr, *d_kpair_idx = nullptr;
+  const int32_t* d_unit_shift = nullptr;
 };
 
 namespace {
@@ -200,7 +201,8 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
                     {h.pair_ptr.data(), h.pair_ptr.size() * 4, 0},
                     {h.pair_idx.data(), h.pair_idx.size() * 4, 0},
                     {h.kpair_ptr.data(), h.kpair_ptr.size() * 4, 0},
-                    {h.kpair_idx.data(), h.kpair_idx.size() * 4, 0}};
+                    {h.kpair_idx.data(), h.kpair_idx.size() * 4, 0},
+                    {h.unit_shift.data(), h.unit_shift.size() * 4, 0}};
     size_t total = 0;
     for (Part& part : parts) {
       part.off = total;
@@ -234,6 +236,7 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->d_pair_idx = reinterpret_cast<const int32_t*>(base + parts[10].off);
     p->d_kpair_ptr = reinterpret_cast<const int32_t*>(base + parts[11].off);
     p->d_kpair_idx = reinterpret_cast<const int32_t*>(base + parts[12].off);
+    p->d_unit_shift = reinterpret_cast<const int32_t*>(base + parts[13].off);
     p->on_device = true;
   }
   *out = p;
@@ -329,6 +332,7 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
   fp.wg_ptr = p->d_wg_ptr;
   fp.pieces = p->d_pieces;
   fp.combine = p->d_combine;
+  fp.unit_shift = p->d_unit_shift;
   fp.partial = static_cast<float*>(workspace);
   fp.groups = h.fwd_groups;
   fp.n_combine = (int32_t)h.combine.size();

@@ -273,7 +273,15 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int h = unit / p.n_pairs;
     const int pr = unit - h * p.n_pairs;
     const int qrow = pr * UNIT_ROWS + w * 32 + jq;
-    const const_i32p ent = unit_idx + unit_ptr[pr] + e_begin;
+    // entries in the unit's rotated order: tile t of this piece is list entry
+    // (e_begin + t + shift) mod n_unit
+    const const_i32p ulist = unit_idx + unit_ptr[pr];
+    const int n_unit = unit_ptr[pr + 1] - unit_ptr[pr];
+    const int rot = e_begin + ((const_i32p)p.unit_shift)[unit];
+    auto ent_at = [&](int t) {
+      const int j = rot + t;
+      return ulist[j >= n_unit ? j - n_unit : j];
+    };
     const int n_ent = e_end - e_begin;
     lc.k_cache_h = p.k_cache + (int64_t)h * p.cache_cap * D;
     lc.v_cache_h = p.v_cache + (int64_t)h * p.cache_cap * D;
@@ -305,8 +313,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
       issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
       if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
     };
-    if (n_ent > 0) issue_tile(ent[0] >> 4, sbuf0, skd0);
-    if (n_ent > 1) issue_tile(ent[1] >> 4, sbuf1, skd1);
+    if (n_ent > 0) issue_tile(ent_at(0) >> 4, sbuf0, skd0);
+    if (n_ent > 1) issue_tile(ent_at(1) >> 4, sbuf1, skd1);
 
     // Tiles go in pairs: iteration j computes tiles 2j, 2j+1 (buffers of one
     // half of the ring) after issuing tiles 2j+2, 2j+3 into the other half,
@@ -320,8 +328,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
       // the four entries this pair needs, read before the barrier (their
       // scalar-load latency then overlaps the wait instead of following it)
       const int last = n_ent - 1;
-      const int e0 = ent[t], e1 = ent[min(t + 1, last)];
-      int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
+      const int e0 = ent_at(t), e1 = ent_at(min(t + 1, last));
+      int e2 = ent_at(min(t + 2, last)), e3 = ent_at(min(t + 3, last));
       // (pin the loads here: otherwise they are rematerialised after the barrier)
       asm volatile("" : "+s"(e2), "+s"(e3));
       wait_vm_all();  // this wave's loads of tiles t, t+1 (the only ones in flight)

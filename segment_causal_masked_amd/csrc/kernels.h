@@ -31,6 +31,7 @@ struct FwdParams {
   const int32_t* wg_ptr;   // groups+1: pieces of each persistent workgroup
   const int4* pieces;      // {unit, entry_begin, entry_end, slot or -1}
   const int4* combine;     // {unit, first_slot, n_pieces, 0}
+  const int32_t* unit_shift;  // per unit: entries visited in order (j + shift) mod n
   float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
   int64_t q_stride, kv_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;

@@ -353,6 +353,27 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
       p.combine.push_back(CombineItem{int32_t(u), first_slot, made, 0});
     }
   }
+  // Rotation: the largest piece of each unit is aligned so that at time tau of
+  // its workgroup's range (tiles already done by that workgroup) it visits
+  // entry tau mod n.  The workgroups of an XCD (consecutive ranges, the same
+  // heads) then stream the same key tiles at about the same time and share
+  // them in that XCD's L2, instead of each walking its own offset.
+  p.unit_shift.assign(size_t(n_units), 0);
+  for (int64_t u = 0; u < n_units; ++u) {
+    const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
+    const int64_t n = p.pair_ptr[size_t(pr + 1)] - p.pair_ptr[size_t(pr)];
+    if (n == 0) continue;
+    const int64_t start = h * row_total + p.pair_ptr[size_t(pr)];
+    const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
+    int64_t best_g = g0, best_len = -1;
+    for (int64_t g = g0; g <= g1; ++g) {
+      const int64_t a = std::max(bound(g), start), b = std::min(bound(g + 1), start + n);
+      if (b - a > best_len) best_len = b - a, best_g = g;
+    }
+    // at local index j the workgroup has done (start + j - bound(best_g)) tiles
+    const int64_t shift = (start - bound(best_g)) % n;
+    p.unit_shift[size_t(u)] = int32_t((shift + n) % n);
+  }
   p.wg_ptr.assign(size_t(groups) + 1, 0);
   for (int32_t g = 0; g < groups; ++g) {
     p.pieces.insert(p.pieces.end(), per[size_t(g)].begin(), per[size_t(g)].end());

@@ -73,6 +73,9 @@ struct HostPlan {
   std::vector<Piece> pieces;
   std::vector<CombineItem> combine;
   int32_t n_slots = 0;
+  // per unit: its entries are visited in the rotated order
+  // (j + unit_shift) mod n for j = 0 .. n - 1; pieces are ranges of j
+  std::vector<int32_t> unit_shift;
   // backward schedule (build_bwd_schedule): per pair of key tiles (2 u,
   // 2 u + 1) the union of their non-empty q-tiles, entry = (q_tile << 4) |
   // flags with bit 0 / 1 = mask for the first / second key tile (PARTIAL,
