@@ -10,10 +10,11 @@
 // Three launches on one stream:
 //   1. bwd_rowstats_kernel: delta and lse * log2(e) per (head, query);
 //   2. bwd_dkdv_kernel: one workgroup per pair of 64-key tiles of a head
-//      (four waves, 32 keys each, one wave per SIMD), looping over the
-//      q-tiles that see those keys (the union of the two key tiles' column
-//      lists); 128-query tiles of Q, dO and the row statistics are staged in
-//      LDS, double buffered; dK and dV accumulate in registers;
+//      (eight waves, two per SIMD: four key groups of 32 keys x two halves of
+//      each q-tile), looping over the q-tiles that see those keys (the union
+//      of the two key tiles' column lists); 128-query tiles of Q, dO and the
+//      row statistics are staged in LDS, double buffered; dK and dV
+//      accumulate in registers and the two halves are summed at the end;
 //   3. bwd_dq_kernel: one workgroup per pair of 128-query tiles (eight waves,
 //      32 queries each) looping over the forward's key-tile lists, with K / V
 //      tiles staged as in the forward; dQ accumulates in registers.
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
 // 2. dK, dV
 // ---------------------------------------------------------------------------
 
-constexpr int KV_WAVES = 4;
+constexpr int KV_WAVES = 8;
 constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int QT_ROWS = 128;
 constexpr int QTILE_BYTES = QT_ROWS * D * 2;         // 32 KB: a 128-row Q or dO tile
@@ -89,26 +90,22 @@ constexpr int GRP128 = QT_ROWS * 64;                 // chunk-group stride of su
 constexpr int STAT_OFF = 2 * QTILE_BYTES;            // lse2[128] | delta[128]
 constexpr int QD_OFF = STAT_OFF + 2 * QT_ROWS * 4;   // qdesc[128]
 constexpr int KV_STAGE_BYTES = QD_OFF + QT_ROWS * 16;
+static_assert(KV_STAGE_BYTES >= 4 * 64 * 64 * 4, "a stage holds one dV or dK half for the final sum");
 
 // Stage q-tile qt of head h: Q and dO rows (rows past nq read row nq - 1:
-// masked), lse2 / delta, query descriptors.  Wave w fills row groups 2 w and
-// 2 w + 1 of both tiles (8 + 8 loads); wave 0 also the statistics, wave 1 the
-// descriptors.
+// masked), lse2 / delta, query descriptors.  Wave w fills row group w of both
+// tiles (4 + 4 loads); wave 0 also the statistics, wave 1 the descriptors.
 __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt, char* stg,
                                                int w, int lane) {
   const int r_in = lane >> 2;
   const int cl = (lane & 3) ^ ((lane >> 4) & 3);
+  int row = qt * QT_ROWS + 16 * w + r_in;
+  row = row < p.nq ? row : p.nq - 1;
+  const int64_t off = (int64_t)row * p.q_stride + (int64_t)h * D + 8 * cl;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rg = 2 * w + j;
-    int row = qt * QT_ROWS + 16 * rg + r_in;
-    row = row < p.nq ? row : p.nq - 1;
-    const int64_t off = (int64_t)row * p.q_stride + (int64_t)h * D + 8 * cl;
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      dma16(p.q + off + 32 * cg, stg + cg * GRP128 + rg * 1024);
-      dma16(p.d_o + off + 32 * cg, stg + QTILE_BYTES + cg * GRP128 + rg * 1024);
-    }
+  for (int cg = 0; cg < 4; ++cg) {
+    dma16(p.q + off + 32 * cg, stg + cg * GRP128 + w * 1024);
+    dma16(p.d_o + off + 32 * cg, stg + QTILE_BYTES + cg * GRP128 + w * 1024);
   }
   const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + (int64_t)qt * QT_ROWS;
   if (w == 0) {
@@ -132,13 +129,30 @@ struct KvWave {
   int tbase[2];   // transpose-read base for rows +0 / +4
 };
 
-// One staged q-tile against this wave's 32 keys.
-template <bool MASKED>
-__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, float scale_log2, int hh) {
+// Visibility of this wave's 64 queries of the staged q-tile (query blocks
+// 2 qh, 2 qh + 1) for this lane's key, in score-register order: bit 16 bb + i
+// <-> query 32 (2 qh + bb) + 16 (i / 8) + 8 hh + i % 8.  PARTIAL tiles only.
+__device__ __forceinline__ uint32_t kv_vis_bits(const char* stg, int kseg, uint32_t kbits, int hh,
+                                                int qh) {
+  uint32_t v = 0;
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    const int ql = 32 * (2 * qh + (j >> 4)) + 16 * ((j >> 3) & 1) + 8 * hh + (j & 7);
+    const QDescDev qd = *reinterpret_cast<const QDescDev*>(stg + QD_OFF + 16 * ql);
+    v |= (uint32_t)visible(qd, kseg, kbits) << j;
+  }
+  return v;
+}
+
+// This wave's half of a staged q-tile (query blocks 2 qh, 2 qh + 1) against
+// its 32 keys; vis = all ones on FULL tiles.
+__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, uint32_t vis,
+                                         float scale_log2, int hh, int qh) {
   const char* qtile = stg;
   const char* dotile = stg + QTILE_BYTES;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int bb = 0; bb < 2; ++bb) {
+    const int b = 2 * qh + bb;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -149,27 +163,21 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, float scal
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, st.vf[ks], dp, 0, 0, 0);
     }
     // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8
-    float l2[16], dl[16];
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
       const float4 lv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
       const float4 dv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
-      l2[4 * g + 0] = lv.x; l2[4 * g + 1] = lv.y; l2[4 * g + 2] = lv.z; l2[4 * g + 3] = lv.w;
-      dl[4 * g + 0] = dv.x; dl[4 * g + 1] = dv.y; dl[4 * g + 2] = dv.z; dl[4 * g + 3] = dv.w;
-    }
-    bf16x8 pb[2], dsb[2];
+      const float l2[4] = {lv.x, lv.y, lv.z, lv.w}, dl[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -l2[i]));
-      if (MASKED) {
-        const int ql = 32 * b + 16 * (i >> 3) + 8 * hh + (i & 7);
-        const QDescDev qd = *reinterpret_cast<const QDescDev*>(stg + QD_OFF + 16 * ql);
-        pv = visible(qd, st.kseg, st.kbits) ? pv : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -l2[r]));
+        pv = ((vis >> (16 * bb + i)) & 1u) ? pv : 0.f;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl[r]));
       }
-      const float dsv = pv * (dp[i] - dl[i]);
-      pb[i >> 3][i & 7] = (__bf16)pv;
-      dsb[i >> 3][i & 7] = (__bf16)dsv;
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -202,8 +210,12 @@ __device__ __forceinline__ void kv_store(uint16_t* dst, const f32x16* acc, float
     }
 }
 
-__global__ __launch_bounds__(KV_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdParams p) {
+// Eight waves, two per SIMD: wave w takes the 32 keys of key group w % 4
+// (64-key tile 2 u + (w % 4) / 2, half (w % 4) % 2) against query blocks
+// 2 (w / 4), 2 (w / 4) + 1 of every staged q-tile; the two waves of a key
+// group (one per SIMD pair... w and w + 4) add their dK / dV through LDS at
+// the end.
+__global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char stg0[KV_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stg1[KV_STAGE_BYTES];
 
@@ -211,11 +223,12 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
+  const int kg = w & 3, qh = w >> 2;
   const int unit = blockIdx.x;                 // h * n_kpairs + u
   const int h = unit / p.n_kpairs;
   const int u = unit - h * p.n_kpairs;
-  const int sub = w >> 1;                      // which key tile of the pair
-  const int key = (2 * u + sub) * BK + 32 * (w & 1) + jq;
+  const int sub = kg >> 1;                     // which key tile of the pair
+  const int key = (2 * u + sub) * BK + 32 * (kg & 1) + jq;
   const float scale_log2 = p.scale_log2;
 
   KvWave st;
@@ -230,7 +243,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
     // the second key tile of the last pair may not exist (its entries are
     // all EMPTY for these waves)
-    const KDescDev kd = 2 * u + sub < p.nkt ? p.kdesc[(2 * u + sub) * BK + 32 * (w & 1) + jq]
+    const KDescDev kd = 2 * u + sub < p.nkt ? p.kdesc[(2 * u + sub) * BK + 32 * (kg & 1) + jq]
                                             : KDescDev{-1, 0u};
     st.kseg = kd.seg;
     st.kbits = kd.bits;
@@ -256,8 +269,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   auto compute = [&](int t, const char* stg) __attribute__((always_inline)) {
     const int e = ent[t];
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
-    if ((e >> sub) & 1) kv_qtile<true>(st, stg, scale_log2, hh);
-    else kv_qtile<false>(st, stg, scale_log2, hh);
+    // one code path for FULL and PARTIAL tiles (FULL: all bits set)
+    const uint32_t vis = ((e >> sub) & 1) ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
+    kv_qtile(st, stg, vis, scale_log2, hh, qh);
   };
   if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
   for (int t = 0; t < n_ent; t += 2) {
@@ -273,10 +287,34 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  if (key < p.nk) {
-    const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * D;
-    kv_store(p.dv + off, st.dv, 1.f, hh);
-    kv_store(p.dk + off, st.dk, p.scale, hh);
+  // dK, dV of a key group = the sum of its two waves' halves: the upper waves
+  // hand theirs over through the (now idle) stage buffers.
+  lds_barrier();
+  float* xv = reinterpret_cast<float*>(stg0) + kg * 4096 + lane;
+  float* xk = reinterpret_cast<float*>(stg1) + kg * 4096 + lane;
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ri = 0; ri < 16; ++ri) {
+        xv[(16 * db + ri) * 64] = st.dv[db][ri];
+        xk[(16 * db + ri) * 64] = st.dk[db][ri];
+      }
+  }
+  lds_barrier();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ri = 0; ri < 16; ++ri) {
+        st.dv[db][ri] += xv[(16 * db + ri) * 64];
+        st.dk[db][ri] += xk[(16 * db + ri) * 64];
+      }
+    if (key < p.nk) {
+      const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * D;
+      kv_store(p.dv + off, st.dv, 1.f, hh);
+      kv_store(p.dk + off, st.dk, p.scale, hh);
+    }
   }
 }
 
