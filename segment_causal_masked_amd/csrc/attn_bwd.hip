@@ -41,6 +41,16 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Workgroup b is dispatched to XCD b % 8.  Map it to unit
+// (b % 8) * ceil(G / 8) + b / 8, so that each XCD works through a contiguous
+// range of units -- neighbouring tiles of the same head, whose Q / dO or K / V
+// tiles then meet in that XCD's L2 -- instead of every eighth unit.
+__device__ __forceinline__ int xcd_major_unit(int b, int G) {
+  const int per = (G + 7) >> 3;
+  const int u = (b & 7) * per + (b >> 3);
+  return u;
+}
+
 // ---------------------------------------------------------------------------
 // 1. row statistics
 // ---------------------------------------------------------------------------
@@ -224,7 +234,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
   const int kg = w & 3, qh = w >> 2;
-  const int unit = blockIdx.x;                 // h * n_kpairs + u
+  const int unit = xcd_major_unit(blockIdx.x, (int)gridDim.x);  // h * n_kpairs + u
+  if (unit >= p.heads * p.n_kpairs) return;
   const int h = unit / p.n_kpairs;
   const int u = unit - h * p.n_kpairs;
   const int sub = kg >> 1;                     // which key tile of the pair
@@ -425,7 +436,8 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
   const int half = w >> 2;  // which q-tile of the pair
-  const int unit = blockIdx.x;
+  const int unit = xcd_major_unit(blockIdx.x, (int)gridDim.x);
+  if (unit >= p.heads * p.n_pairs) return;
   const int h = unit / p.n_pairs;
   const int pr = unit - h * p.n_pairs;
   const int qrow = pr * 256 + w * 32 + jq;
@@ -537,13 +549,15 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (p.nk > 0 && p.n_kpairs > 0) {
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(p.heads * p.n_kpairs)), dim3(KV_THREADS),
+    const int units = p.heads * p.n_kpairs;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(8 * ((units + 7) / 8))), dim3(KV_THREADS),
                        0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.nq > 0 && p.n_pairs > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(p.heads * p.n_pairs)), dim3(Q_THREADS), 0,
+    const int units = p.heads * p.n_pairs;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(8 * ((units + 7) / 8))), dim3(Q_THREADS), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
