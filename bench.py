@@ -169,7 +169,8 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
     t0 = time.perf_counter()
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    A = plan.info().unmasked_pairs
+    pinfo = plan.info()
+    A = pinfo.unmasked_pairs
     qs = [rnd(w.n_q) for _ in range(4)]
     ks = [rnd(w.n_new) for _ in range(4)]
     vs = [rnd(w.n_new) for _ in range(4)]
@@ -195,8 +196,8 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
             sess_ms.append(ev[0].elapsed_time(ev[5]))
     c, a = float(np.mean(call_ms)), float(np.mean(app_ms))
     app_bytes = 2 * 2 * w.n_new * H * D * 2
-    kv_bytes = 2 * w.n_keys * H * D * 2
-    return {"workload": w.name, "queries": w.n_q, "keys": w.n_keys, "heads": H,
+    kv_bytes = 2 * pinfo.n_keys * H * D * 2   # keys the call reads: cached rows + new tokens
+    return {"workload": w.name, "queries": w.n_q, "keys": int(pinfo.n_keys), "heads": H,
             "unmasked_pairs": A, "plan_host_ms": round(plan_ms, 2),
             "fwd_ms_per_call": round(c, 3),
             "fwd_tflops": round(4.0 * D * H * A / (c * 1e-3) / 1e12, 2),
@@ -340,7 +341,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "queries": w.n_q, "keys": w.n_keys, "heads": H,
+        "config": {"workload": w.name, "queries": w.n_q, "keys": w.n_keys,
+                   "keys_read": int(info.n_keys), "heads": H,
                    "head_dim": D, "cached_segments": n_cached_segs, "denoising_calls": NFE,
                    "layers_per_step": L, "unmasked_pairs": A,
                    "tiles": {"full": info.n_full_tiles, "partial": info.n_partial_tiles,

@@ -234,10 +234,15 @@ nomas_status nomas_attn_bwd(const nomas_plan* plan,
 nomas_status nomas_kvcache_create(int32_t heads, int32_t head_dim, int64_t capacity,
                                   void* k_buf, void* v_buf, nomas_kvcache** out);
 
-/* Append one segment: its tokens' K/V are k_new / v_new [tokens][H][128]
- * (token stride kv_stride) and are copied behind the cached tokens on
- * hip_stream.  Over capacity: NOMAS_ERR_CAPACITY and nothing is written or
- * recorded.  A segment already in the cache: NOMAS_ERR_LAYOUT. */
+/* Append one segment: k_new / v_new hold its tokens' K/V, [tokens][H][128]
+ * (token stride kv_stride) in the segment's token order.  The cache keeps the
+ * rows a later segment can see -- the video and head tokens, which come first
+ * -- and copies them behind the cached rows on hip_stream; the action-tail
+ * and padding rows are not stored (action tails are visible only inside their
+ * own segment, "Model Architecture": Action-Aware Causal Attention).
+ * Capacity is counted in stored rows.  Over capacity: NOMAS_ERR_CAPACITY and
+ * nothing is written or recorded.  A segment already in the cache:
+ * NOMAS_ERR_LAYOUT. */
 nomas_status nomas_kvcache_append(nomas_kvcache* cache, const nomas_segment* seg,
                                   const void* k_new, const void* v_new,
                                   int64_t kv_stride, void* hip_stream);
@@ -247,6 +252,7 @@ nomas_status nomas_kvcache_append(nomas_kvcache* cache, const nomas_segment* seg
 nomas_status nomas_kvcache_truncate(nomas_kvcache* cache, int32_t n_segments);
 
 nomas_status nomas_kvcache_reset(nomas_kvcache* cache);
+/* n_tokens: stored rows (video + head tokens of the cached segments). */
 nomas_status nomas_kvcache_len(const nomas_kvcache* cache, int64_t* n_tokens,
                                int32_t* n_segments);
 nomas_status nomas_kvcache_destroy(nomas_kvcache* cache);

@@ -458,7 +458,7 @@ nomas_status nomas_kvcache_append(nomas_kvcache* c, const nomas_segment* seg, co
   for (const auto& s : c->segs)
     if (s.video == seg->video && s.index == seg->index)
       return fail(NOMAS_ERR_LAYOUT, "segment already in the cache");
-  const int64_t n = nomas::segment_tokens(*seg);
+  const int64_t n = nomas::segment_cached_tokens(*seg);  // video + head rows, the first ones
   if (c->len + n > c->capacity) return fail(NOMAS_ERR_CAPACITY, "append would exceed the cache capacity");
   nomas_status s;
   if ((s = check_dev_ptr(k_new, true, "k_new")) || (s = check_dev_ptr(v_new, true, "v_new"))) return s;
@@ -488,7 +488,7 @@ nomas_status nomas_kvcache_truncate(nomas_kvcache* c, int32_t n_segments) {
   c->segs.resize((size_t)n_segments);
   c->serials.resize((size_t)n_segments);
   int64_t len = 0;
-  for (const auto& s : c->segs) len += nomas::segment_tokens(s);
+  for (const auto& s : c->segs) len += nomas::segment_cached_tokens(s);
   c->len = len;
   return ok();
 }

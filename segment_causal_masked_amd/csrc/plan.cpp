@@ -22,6 +22,10 @@ int64_t segment_tokens(const nomas_segment& s) {
   return n;
 }
 
+int64_t segment_cached_tokens(const nomas_segment& s) {
+  return int64_t(s.n_frames) * s.tokens_per_frame + s.n_head;
+}
+
 std::string check_segment(const nomas_segment& s) {
   char buf[256];
   auto fail = [&](const char* what) {
@@ -101,7 +105,9 @@ void q_runs(const nomas_segment& s, int32_t ord, int32_t lo, int mode, int64_t* 
   push(s.n_pad, -1, 0, 0u);
 }
 
-void k_runs(const nomas_segment& s, int32_t ord, int64_t* pos, std::vector<Run>* out) {
+// cached: the segment as a KV cache holds it (video and head tokens only)
+void k_runs(const nomas_segment& s, int32_t ord, int64_t* pos, std::vector<Run>* out,
+            bool cached) {
   auto push = [&](int64_t n, int32_t seg, uint32_t bits) {
     if (n <= 0) return;
     if (!out->empty()) {
@@ -116,6 +122,7 @@ void k_runs(const nomas_segment& s, int32_t ord, int64_t* pos, std::vector<Run>*
     *pos += n;
   };
   push(int64_t(s.n_frames) * s.tokens_per_frame + s.n_head, ord, 0u);
+  if (cached) return;
   for (int a = 0; a < s.n_actions; ++a) push(s.actions[a].n_tokens, ord, 1u << a);
   push(s.n_pad, -1, 0u);
 }
@@ -214,9 +221,9 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   }
   p.nq = pos;
   pos = 0;
-  for (const auto& s : cached) k_runs(s, ord[{s.video, s.index}], &pos, &kr);
+  for (const auto& s : cached) k_runs(s, ord[{s.video, s.index}], &pos, &kr, true);
   p.n_cached = pos;
-  for (const auto& s : kv_new) k_runs(s, ord[{s.video, s.index}], &pos, &kr);
+  for (const auto& s : kv_new) k_runs(s, ord[{s.video, s.index}], &pos, &kr, false);
   p.nk = pos;
   if (p.nq > (int64_t(1) << 30) || p.nk > (int64_t(1) << 30)) {
     *err = "more than 2^30 query or key tokens";

@@ -99,6 +99,10 @@ struct CacheState {
 // Validate one record; returns "" or a description of the problem.
 std::string check_segment(const nomas_segment& s);
 int64_t segment_tokens(const nomas_segment& s);
+// Tokens of a segment that a KV cache keeps: its video and head tokens (the
+// first ones).  Action tails are visible only inside their own segment and
+// padding to nobody, so no later query can see them.
+int64_t segment_cached_tokens(const nomas_segment& s);
 
 // Build the host plan.  keys = cached ++ kv_new.  Returns NOMAS_OK or an
 // error status with *err filled.

@@ -58,6 +58,16 @@ def new_cache(heads, capacity):
     return nm.nomas_kvcache_create(heads, capacity, kb, vb)
 
 
+def stored_rows(segments):
+    """Row indices (into the segments' concatenated tokens) that a KV cache
+    keeps: each segment's video and head tokens, which come first."""
+    rows, off = [], 0
+    for s in segments:
+        rows.append(np.arange(off, off + s.n_frames * s.tokens_per_frame + s.n_head))
+        off += s.n_tokens
+    return np.concatenate(rows) if rows else np.zeros(0, np.int64)
+
+
 def fill_cache(cache, segments, k_tok, v_tok):
     """Append segments one by one from token-major [T,H,D] device tensors."""
     off = 0

@@ -8,7 +8,7 @@ import oracle
 import segment_causal_masked_amd as nm
 from segment_causal_masked_amd import workloads as wl
 from gpu_util import (SCALE, check_lse, check_o, dev, fill_cache, host, need_gpu, new_cache,
-                      run_fwd, say)
+                      run_fwd, say, stored_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,11 +86,15 @@ def test_config3_cached_step_and_append_layout():
     w = wl.config3()
     say("config3 480p cached step: 4 cached segments (13120 keys) + 3280 new, 16 heads")
     cache, kc, vc = build_cached(w)
-    # the append wrote token-major rows into the head-major cache, bit for bit
-    kb = cache.k_buf[:, :w.n_cached].permute(1, 0, 2).contiguous()
-    vb = cache.v_buf[:, :w.n_cached].permute(1, 0, 2).contiguous()
-    assert torch.equal(kb, dev(kc)) and torch.equal(vb, dev(vc))
-    assert nm.nomas_kvcache_len(cache) == (w.n_cached, 4)
+    # the append wrote the video + head rows of each segment (token-major) into
+    # the head-major cache, bit for bit; action tails are not kept
+    rows = stored_rows(w.cached)
+    n = len(rows)
+    assert n == w.n_cached - 4 * 96
+    kb = cache.k_buf[:, :n].permute(1, 0, 2).contiguous()
+    vb = cache.v_buf[:, :n].permute(1, 0, 2).contiguous()
+    assert torch.equal(kb, dev(kc[rows])) and torch.equal(vb, dev(vc[rows]))
+    assert nm.nomas_kvcache_len(cache) == (n, 4)
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
     q, kn, vn = w.q(), w.k_new(), w.v_new()
     o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
@@ -236,9 +240,10 @@ def test_config4_long_session_sampled_rows():
         check_lse(host(l)[heads][:, rows], l_ref, f"config4 call {nfe}")
     nm.nomas_kvcache_append(cache, w.new[0], dev(kn), dev(vn))   # K/V of the last call
     torch.cuda.synchronize()
-    assert nm.nomas_kvcache_len(cache) == (w.n_cached + w.n_new, 17)
-    got = cache.k_buf[:, w.n_cached:].permute(1, 0, 2)
-    assert torch.equal(got, dev(kn))
+    n_old, n_add = len(stored_rows(w.cached)), len(stored_rows(w.new))
+    assert nm.nomas_kvcache_len(cache) == (n_old + n_add, 17)
+    got = cache.k_buf[:, n_old:n_old + n_add].permute(1, 0, 2)
+    assert torch.equal(got, dev(kn[stored_rows(w.new)]))
 
 
 def test_config5_training_pack_forward_sampled():
