@@ -111,7 +111,7 @@ def bench_training(nm, wl, torch, iters=5, warmup=2):
     """Forward + backward on the 131072-token training pack (4 videos, 16 heads):
     mean time of each over `iters` calls after `warmup`, HIP events on the
     launch stream.  Inputs are drawn on the device (timing only)."""
-    w = wl.config5()
+    w = wl.training_pack_131k()
     H, D = w.heads, 128
     t0 = time.perf_counter()
     plan = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=H)
@@ -155,7 +155,7 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
     segment; per session 4 forward calls with fresh Q / K_new / V_new, then the
     append of the new segment (rolled back after each session).  Inputs are
     drawn on the device (timing only)."""
-    w = wl.config4()
+    w = wl.long_session_720p()
     H, D = w.heads, 128
     g = torch.Generator(device="cuda")
     g.manual_seed(4000)
@@ -233,7 +233,7 @@ def main():
 
     nm.load()
     torch.cuda.set_device(0)
-    w = wl.config3()
+    w = wl.cached_step_480p()
     H, D, L, NFE = w.heads, 128, args.layers, 4
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(torch.bfloat16)
 

@@ -18,9 +18,10 @@ Shapes follow the Hy-Nomas pages:
 Token order inside a segment (the pages leave it open):
     [video, frame-major | head | a_0 | a_1 | ... | trailing pad]
 
-Random numbers come from numpy's PCG64 with seed = 1000*config + tensor id
-(Q=1, K=2, V=3, dO=4, windows=5, cache=6; the n-th of several denoising calls
-adds 10*n).  Values are N(0,1) rounded to bf16 (round-to-nearest-even) except
+Random numbers come from numpy's PCG64 with seed = the workload's seed base
+(1000, 2000, 3000, 4000, 5000 for the five workloads below, in order) + tensor
+id (Q=1, K=2, V=3, dO=4, windows=5, cache=6; the n-th of several denoising
+calls adds 10*n).  Values are N(0,1) rounded to bf16 (round-to-nearest-even) except
 the tiny fp32 case.
 """
 from __future__ import annotations
@@ -177,7 +178,7 @@ class Workload:
         return k, v
 
 
-def config1() -> Workload:
+def tiny_two_segments() -> Workload:
     """Tiny case: 1 head, fp32; 2 segments of 2 frames x 4x4 + 8 head + 2 tails
     of 4 tokens with windows [0,1) and [1,2)."""
     segs = [Segment(0, j, 2, 16, 8, [(4, 0, 1), (4, 1, 2)]) for j in range(2)]
@@ -185,7 +186,7 @@ def config1() -> Workload:
                     fp32_inputs=True, seed_base=1000)
 
 
-def config2(seed_set: int = 0) -> Workload:
+def single_segment_480p(seed_set: int = 0) -> Workload:
     """One 480p segment, no cache: 8 x 390 video + 64 head + 3 x 32 tails."""
     g = rng(2000 + TID_WIN + 7919 * seed_set)
     seg = make_segment(g, 0, 0, 8, TPF_480P, 64, 3, 32,
@@ -194,7 +195,7 @@ def config2(seed_set: int = 0) -> Workload:
                     seed_base=2000)
 
 
-def config3(seed_set: int = 0, n_cached: int = 4) -> Workload:
+def cached_step_480p(seed_set: int = 0, n_cached: int = 4) -> Workload:
     """480p cached step: 4 cached segments + 1 new one (queries)."""
     g = rng(3000 + TID_WIN + 7919 * seed_set)
     segs = [make_segment(g, 0, j, 8, TPF_480P, 64, 3, 32,
@@ -204,7 +205,7 @@ def config3(seed_set: int = 0, n_cached: int = 4) -> Workload:
                     segs[:-1], [segs[-1]], seed_base=3000)
 
 
-def config4(seed_set: int = 0, n_cached: int = 16) -> Workload:
+def long_session_720p(seed_set: int = 0, n_cached: int = 16) -> Workload:
     """720p long session: 16 cached segments + 1 new; 4 denoising calls."""
     g = rng(4000 + TID_WIN + 7919 * seed_set)
     segs = [make_segment(g, 0, j, 8, TPF_720P, 64, 4, 32,
@@ -240,7 +241,7 @@ def pack_layout(g, n_videos, tokens_per_video, seg_range=(4, 8), tpf=TPF_480P,
     return out
 
 
-def config5(seed_set: int = 0) -> Workload:
+def training_pack_131k(seed_set: int = 0) -> Workload:
     """Training pack of 131072 tokens: 4 videos x 32768, 4-8 segments each."""
     g = rng(5000 + TID_WIN + 7919 * seed_set)
     segs = pack_layout(g, 4, 32768)
@@ -258,4 +259,6 @@ def small_pack(seed: int = 0, n_videos: int = 2, tokens_per_video: int = 2048,
                     seed_base=5500 + 100 * seed)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"tiny_two_segments": tiny_two_segments, "single_segment_480p": single_segment_480p,
+             "cached_step_480p": cached_step_480p, "long_session_720p": long_session_720p,
+             "training_pack_131k": training_pack_131k}

@@ -26,7 +26,7 @@ def host_plan(q, kv, heads=1, mode="R", bq=0, bk=0):
     return nm.nomas_attn_plan(q, kv, heads=heads, mode=mode, host_only=True, block_q=bq, block_k=bk)
 
 
-@pytest.mark.parametrize("name", ["config1_mask.txt", "pack2_mask.txt"])
+@pytest.mark.parametrize("name", ["tiny_two_segments_mask.txt", "pack2_mask.txt"])
 def test_plan_matches_hand_built_fixtures(name):
     segs, mask, A, (bq, bk), tmap = load_mask_fixture(name)
     for mode in ("R", "K", "H"):
@@ -52,9 +52,11 @@ def test_plan_classes_random_layouts_and_tiles():
         assert p.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk, mode)
 
 
-@pytest.mark.parametrize("cfg,mode", [(1, "R"), (2, "R"), (2, "K"), (2, "H"), (3, "R"), (3, "H")])
-def test_plan_classes_configs(cfg, mode):
-    w = wl.CONFIGS[cfg]()
+@pytest.mark.parametrize("name,mode", [("tiny_two_segments", "R"), ("single_segment_480p", "R"),
+                                       ("single_segment_480p", "K"), ("single_segment_480p", "H"),
+                                       ("cached_step_480p", "R"), ("cached_step_480p", "H")])
+def test_plan_classes_workloads(name, mode):
+    w = wl.WORKLOADS[name]()
     keys = w.cached + w.new
     p = host_plan(w.q_layout, keys, heads=w.heads, mode=mode)
     info = p.info()
@@ -67,8 +69,8 @@ def test_plan_classes_configs(cfg, mode):
 
 
 @pytest.mark.slow
-def test_plan_classes_config4_full():
-    w = wl.config4()
+def test_plan_classes_long_session_720p_full():
+    w = wl.long_session_720p()
     keys = w.cached + w.new
     p = host_plan(w.q_layout, keys, heads=16)
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
@@ -77,8 +79,8 @@ def test_plan_classes_config4_full():
     assert p.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk)
 
 
-def test_plan_classes_config5_sampled_tiles():
-    w = wl.config5()
+def test_plan_classes_training_pack_sampled_tiles():
+    w = wl.training_pack_131k()
     p = host_plan(w.q_layout, w.new, heads=16)
     t = oracle.expand(w.q_layout)
     cls = nm.nomas_plan_export_classes(p)

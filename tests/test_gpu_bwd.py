@@ -72,10 +72,10 @@ def full_case(segs, heads, seed, mode="R", check_heads=None, fp32=False):
     return host(dq), host(dk), host(dv)
 
 
-def test_config1_tiny_backward():
+def test_tiny_two_segments_backward():
     need_gpu()
-    w = wl.config1()
-    say("config1 tiny: 96 tokens, 1 head, backward")
+    w = wl.tiny_two_segments()
+    say("tiny two segments: 96 tokens, 1 head, backward")
     full_case(w.q_layout, 1, 8100)
 
 
@@ -135,20 +135,20 @@ def test_backward_ignores_masked_upstream_rows_bitwise():
 
 
 @pytest.mark.timeout(600)
-def test_config5_training_pack_backward_slice():
+def test_training_pack_131k_backward_slice():
     """Full 131072-token pack on the GPU; the oracle checks the 4096-token slice
     that starts 2048 tokens before video 1's third segment: O, LSE and dQ rows
     of those queries, dK and dV rows of those keys (two heads).  The pack is
     block-diagonal over videos, so the oracle runs on video 1 alone."""
     need_gpu()
-    w = wl.config5()
+    w = wl.training_pack_131k()
     segs = w.q_layout
     starts = np.cumsum([0] + [s.n_tokens for s in segs])
     v1 = [i for i, s in enumerate(segs) if s.video == 1]
     t_seg2 = int(starts[v1[2]])
     t0 = t_seg2 - 2048
     v_lo, v_hi = int(starts[v1[0]]), int(starts[v1[-1] + 1])
-    say(f"config5: {w.n_q} tokens; slice [{t0}, {t0 + 4096}) inside video 1 [{v_lo}, {v_hi})")
+    say(f"training pack: {w.n_q} tokens; slice [{t0}, {t0 + 4096}) inside video 1 [{v_lo}, {v_hi})")
     assert v_lo <= t0 and t0 + 4096 <= v_hi
     plan = nm.nomas_attn_plan(segs, segs, heads=16)
     q, k, v, d_o = w.q(), w.k_new(), w.v_new(), w.d_o()
@@ -163,10 +163,10 @@ def test_config5_training_pack_backward_slice():
     vs = slice(v_lo, v_hi)
     rows = sl - v_lo
     o_ref, l_ref = oracle.forward(q[vs], k[vs], v[vs], tq, tq, SCALE, rows=rows, heads=heads)
-    check_o(host(o)[sl][:, heads], o_ref, "config5 O slice")
-    check_lse(host(lse)[heads][:, sl], l_ref, "config5 LSE slice")
+    check_o(host(o)[sl][:, heads], o_ref, "training pack O slice")
+    check_lse(host(lse)[heads][:, sl], l_ref, "training pack LSE slice")
     dq_ref, dk_ref, dv_ref = oracle.backward(q[vs], k[vs], v[vs], d_o[vs], tq, tq, SCALE,
                                              heads=heads, q_rows=rows, k_rows=rows)
-    check_grad(host(dq)[sl][:, heads], dq_ref, "config5 dQ slice")
-    check_grad(host(dk)[sl][:, heads], dk_ref, "config5 dK slice")
-    check_grad(host(dv)[sl][:, heads], dv_ref, "config5 dV slice")
+    check_grad(host(dq)[sl][:, heads], dq_ref, "training pack dQ slice")
+    check_grad(host(dk)[sl][:, heads], dk_ref, "training pack dK slice")
+    check_grad(host(dv)[sl][:, heads], dv_ref, "training pack dV slice")

@@ -32,10 +32,10 @@ def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None):
     return oracle.forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads)
 
 
-def test_config1_tiny_fp32_inputs():
+def test_tiny_two_segments_fp32_inputs():
     need_gpu()
-    w = wl.config1()
-    say("config1 tiny: 96 tokens, 1 head, fp32 inputs rounded to bf16 for the kernel")
+    w = wl.tiny_two_segments()
+    say("tiny two segments: 96 tokens, 1 head, fp32 inputs rounded to bf16 for the kernel")
     plan, q, k, v, keys = dense_case(w)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 1)
     o_ref, l_ref = oracle_fwd(w, q, k, v, keys)            # oracle on the fp32 inputs
@@ -48,27 +48,27 @@ def test_config1_tiny_fp32_inputs():
 
 
 @pytest.mark.parametrize("mode", ["R", "K", "H"])
-def test_config2_single_segment(mode):
+def test_single_segment_480p(mode):
     need_gpu()
-    w = wl.config2()
-    say(f"config2 single 480p segment, 3280 tokens x 16 heads, mode {mode}")
+    w = wl.single_segment_480p()
+    say(f"single 480p segment, 3280 tokens x 16 heads, mode {mode}")
     plan, q, k, v, keys = dense_case(w, mode)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     heads = None if mode == "R" else [0, 7, 15]
     o_ref, l_ref = oracle_fwd(w, q, k, v, keys, mode=mode, heads=heads)
     hsel = slice(None) if heads is None else heads
-    check_o(host(o)[:, hsel], o_ref, f"config2 {mode}")
-    check_lse(host(l)[hsel], l_ref, f"config2 {mode}")
+    check_o(host(o)[:, hsel], o_ref, f"single segment {mode}")
+    check_lse(host(l)[hsel], l_ref, f"single segment {mode}")
 
 
-def test_config2_sorted_windows_seed_set():
+def test_single_segment_480p_sorted_windows():
     need_gpu()
-    w = wl.config2(seed_set=1)
+    w = wl.single_segment_480p(seed_set=1)
     plan, q, k, v, keys = dense_case(w)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     o_ref, l_ref = oracle_fwd(w, q, k, v, keys, heads=[3, 12])
-    check_o(host(o)[:, [3, 12]], o_ref, "config2 sorted windows")
-    check_lse(host(l)[[3, 12]], l_ref, "config2 sorted windows")
+    check_o(host(o)[:, [3, 12]], o_ref, "single segment, sorted windows")
+    check_lse(host(l)[[3, 12]], l_ref, "single segment, sorted windows")
 
 
 def build_cached(w, layer=0):
@@ -81,10 +81,10 @@ def build_cached(w, layer=0):
     return cache, kc, vc
 
 
-def test_config3_cached_step_and_append_layout():
+def test_cached_step_480p_and_append_layout():
     need_gpu()
-    w = wl.config3()
-    say("config3 480p cached step: 4 cached segments (13120 keys) + 3280 new, 16 heads")
+    w = wl.cached_step_480p()
+    say("480p cached step: 4 cached segments (13120 tokens, 12736 stored rows) + 3280 new, 16 heads")
     cache, kc, vc = build_cached(w)
     # the append wrote the video + head rows of each segment (token-major) into
     # the head-major cache, bit for bit; action tails are not kept
@@ -100,14 +100,14 @@ def test_config3_cached_step_and_append_layout():
     o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
     keys = w.cached + w.new
     o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys)
-    check_o(host(o), o_ref, "config3")
-    check_lse(host(l), l_ref, "config3")
+    check_o(host(o), o_ref, "480p cached step")
+    check_lse(host(l), l_ref, "480p cached step")
 
 
-def test_config3_cached_equals_full_sequence_bitwise():
+def test_cached_step_equals_full_sequence_bitwise():
     """Cached decoding of the last segment == its rows of the full-sequence run."""
     need_gpu()
-    w = wl.config3()
+    w = wl.cached_step_480p()
     cache, kc, vc = build_cached(w)
     q, kn, vn = w.q(), w.k_new(), w.v_new()
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
@@ -134,7 +134,7 @@ def test_config3_cached_equals_full_sequence_bitwise():
 
 def test_masked_kv_perturbation_is_invisible_bitwise():
     need_gpu()
-    w = wl.config2()
+    w = wl.single_segment_480p()
     plan, q, k, v, keys = dense_case(w)
     o0, l0 = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     s = w.q_layout[0]
@@ -196,7 +196,7 @@ def test_single_token_and_empty_query():
 
 def test_stale_plan_after_append_and_truncate():
     need_gpu()
-    w = wl.config3(n_cached=2)
+    w = wl.cached_step_480p(n_cached=2)
     cache, kc, vc = build_cached(w)
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
     q, kn, vn = dev(w.q()), dev(w.k_new()), dev(w.v_new())
@@ -218,12 +218,12 @@ def test_stale_plan_after_append_and_truncate():
     assert torch.equal(before, small.k_buf)
 
 
-def test_config4_long_session_sampled_rows():
-    """Full 720p session shape (16 cached segments, 122944 keys), 4 denoising
+def test_long_session_720p_sampled_rows():
+    """Full 720p session shape (16 cached segments, 113664 stored rows), 4 denoising
     calls, then the append; outputs checked on sampled rows and heads."""
     need_gpu()
-    w = wl.config4()
-    say("config4 720p: 16 cached x 7232 + 7232 new = 122944 keys, 4 calls")
+    w = wl.long_session_720p()
+    say("720p long session: 16 cached x 7104 stored rows + 7232 new = 120896 keys, 4 calls")
     cache, kc, vc = build_cached(w)
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
     keys = w.cached + w.new
@@ -236,8 +236,8 @@ def test_config4_long_session_sampled_rows():
         o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
         o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
                                   rows=rows, heads=heads)
-        check_o(host(o)[rows][:, heads], o_ref, f"config4 call {nfe}")
-        check_lse(host(l)[heads][:, rows], l_ref, f"config4 call {nfe}")
+        check_o(host(o)[rows][:, heads], o_ref, f"720p long session call {nfe}")
+        check_lse(host(l)[heads][:, rows], l_ref, f"720p long session call {nfe}")
     nm.nomas_kvcache_append(cache, w.new[0], dev(kn), dev(vn))   # K/V of the last call
     torch.cuda.synchronize()
     n_old, n_add = len(stored_rows(w.cached)), len(stored_rows(w.new))
@@ -246,14 +246,14 @@ def test_config4_long_session_sampled_rows():
     assert torch.equal(got, dev(kn[stored_rows(w.new)]))
 
 
-def test_config5_training_pack_forward_sampled():
+def test_training_pack_131k_forward_sampled():
     need_gpu()
-    w = wl.config5()
-    say("config5 training pack: 131072 tokens, 4 videos, forward on sampled rows")
+    w = wl.training_pack_131k()
+    say("training pack: 131072 tokens, 4 videos, forward on sampled rows")
     plan, q, k, v, keys = dense_case(w)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     g = np.random.default_rng(55)
     rows = np.sort(g.choice(w.n_q, 48, replace=False))
     o_ref, l_ref = oracle_fwd(w, q, k, v, keys, rows=rows, heads=[0, 13])
-    check_o(host(o)[rows][:, [0, 13]], o_ref, "config5 fwd")
-    check_lse(host(l)[[0, 13]][:, rows], l_ref, "config5 fwd")
+    check_o(host(o)[rows][:, [0, 13]], o_ref, "training pack fwd")
+    check_lse(host(l)[[0, 13]][:, rows], l_ref, "training pack fwd")

@@ -21,7 +21,7 @@ def rand(shape, seed):
 
 
 def test_one_hot_values_reveal_softmax_rows():
-    w = wl.config1()
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     n = len(t)
     q, k = w.q(), w.k_new()
@@ -88,7 +88,7 @@ def test_padding_rows_are_zero_with_minus_inf_lse():
 
 
 def test_output_is_linear_in_values():
-    w = wl.config1()
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     q, k, v = w.q(), w.k_new(), w.v_new()
     o1, _ = oracle.forward(q, k, v, t, t, SCALE)
@@ -163,7 +163,7 @@ def test_backward_row_subsets_match_full():
 # ----------------------------------------------------------------------------
 
 def test_invariant_masked_kv_perturbation_changes_nothing():
-    w = wl.config1()
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     m = oracle.visible_mask(t, t)
     q, k, v = w.q(), w.k_new().astype(np.float64), w.v_new().astype(np.float64)
@@ -179,7 +179,7 @@ def test_invariant_masked_kv_perturbation_changes_nothing():
 
 
 def test_invariant_segment_unaffected_by_next_segment():
-    w = wl.config1()
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     q, k, v = w.q(), w.k_new().astype(np.float64), w.v_new().astype(np.float64)
     o0, _ = oracle.forward(q, k, v, t, t, SCALE)
@@ -190,7 +190,7 @@ def test_invariant_segment_unaffected_by_next_segment():
 
 
 def test_invariant_cached_decoding_equals_full_sequence():
-    w = wl.config3()
+    w = wl.cached_step_480p()
     w.cached = w.cached[:2]                    # keep it quick: 2 cached + new
     full = w.cached + w.new
     tf = oracle.expand(full)
@@ -208,7 +208,7 @@ def test_invariant_cached_decoding_equals_full_sequence():
 
 
 def test_invariant_action_tail_locality_and_non_vacuity():
-    w = wl.config1()
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     q, k, v = w.q(), w.k_new().astype(np.float64), w.v_new().astype(np.float64)
     o0, _ = oracle.forward(q, k, v, t, t, SCALE)

@@ -14,7 +14,7 @@ from segment_causal_masked_amd import workloads as wl
 from golden_io import load_mask_fixture
 
 
-@pytest.mark.parametrize("name", ["config1_mask.txt", "pack2_mask.txt"])
+@pytest.mark.parametrize("name", ["tiny_two_segments_mask.txt", "pack2_mask.txt"])
 def test_hand_built_mask_mode_r(name):
     segs, mask, A, tiles, tmap = load_mask_fixture(name)
     t = oracle.expand(segs)
@@ -23,7 +23,7 @@ def test_hand_built_mask_mode_r(name):
     assert int(m.sum()) == A["R"]
 
 
-@pytest.mark.parametrize("name", ["config1_mask.txt", "pack2_mask.txt"])
+@pytest.mark.parametrize("name", ["tiny_two_segments_mask.txt", "pack2_mask.txt"])
 @pytest.mark.parametrize("mode", MODES)
 def test_hand_built_counts_all_modes(name, mode):
     segs, mask, A, tiles, tmap = load_mask_fixture(name)
@@ -31,19 +31,19 @@ def test_hand_built_counts_all_modes(name, mode):
     assert oracle.unmasked_pairs(t, t, mode) == A[mode]
 
 
-@pytest.mark.parametrize("name", ["config1_mask.txt", "pack2_mask.txt"])
+@pytest.mark.parametrize("name", ["tiny_two_segments_mask.txt", "pack2_mask.txt"])
 def test_hand_built_tile_map(name):
     segs, mask, A, (bq, bk), tmap = load_mask_fixture(name)
     t = oracle.expand(segs)
     for mode in MODES:
         got = oracle.tile_classes(t, t, bq, bk, mode)
-        if name == "config1_mask.txt" or mode == "R":
+        if name == "tiny_two_segments_mask.txt" or mode == "R":
             np.testing.assert_array_equal(got, tmap)
 
 
-def test_config1_workload_matches_fixture():
-    segs, mask, A, _, _ = load_mask_fixture("config1_mask.txt")
-    w = wl.config1()
+def test_tiny_two_segments_workload_matches_fixture():
+    segs, mask, A, _, _ = load_mask_fixture("tiny_two_segments_mask.txt")
+    w = wl.tiny_two_segments()
     t = oracle.expand(w.q_layout)
     np.testing.assert_array_equal(oracle.visible_mask(t, t), mask)
 
@@ -116,9 +116,9 @@ def test_closed_form_A_random():
             assert oracle.unmasked_pairs(t, t, mode) == closed_form_A(segs, mode)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_closed_form_A_configs(cfg):
-    w = wl.CONFIGS[cfg]()
+@pytest.mark.parametrize("name", ["single_segment_480p", "cached_step_480p"])
+def test_closed_form_A_480p_workloads(name):
+    w = wl.WORKLOADS[name]()
     tq, tk = oracle.expand(w.q_layout), oracle.expand(w.cached + w.new)
     got = oracle.unmasked_pairs(tq, tk)
     # keys include cached segments; queries only the new one
