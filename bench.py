@@ -17,10 +17,13 @@ effective FLOPs per call / the call's average duration (HIP events on the
 launch stream), against the bf16 dense MFMA peak of MI355X.
 cpu_baseline = the fp64 oracle on one forward call of the same workload.
 long_session (extra) = the 720p long session: 4 forward calls over 16 cached
-segments + the new one (122,944 keys), then the append.
+segments + the new one (120,896 keys read: the cache keeps video and head
+rows), then the append.
 training_pack (extra, not the headline) = forward and backward times on the
 131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
 (four products) and, beside it, the FlashAttention convention 10 D H A.
+sp8_share (extra) = both rows again at 2 heads, one GPU's share when the 16
+heads are sharded over 8 GPUs.
 """
 from __future__ import annotations
 
@@ -107,12 +110,13 @@ def cpu_baseline(w, runs=3):
             "cpu": cpu_model(), "blas": blas}
 
 
-def bench_training(nm, wl, torch, iters=5, warmup=2):
-    """Forward + backward on the 131072-token training pack (4 videos, 16 heads):
-    mean time of each over `iters` calls after `warmup`, HIP events on the
-    launch stream.  Inputs are drawn on the device (timing only)."""
+def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
+    """Forward + backward on the 131072-token training pack (4 videos, 16 heads,
+    or `heads` of them: one GPU's share when heads are sharded): mean time of
+    each over `iters` calls after `warmup`, HIP events on the launch stream.
+    Inputs are drawn on the device (timing only)."""
     w = wl.training_pack_131k()
-    H, D = w.heads, 128
+    H, D = heads or w.heads, 128
     t0 = time.perf_counter()
     plan = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=H)
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -150,25 +154,32 @@ def bench_training(nm, wl, torch, iters=5, warmup=2):
             "iters": iters}
 
 
-def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
+def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches=1):
     """720p long session: 16 cached segments (7,232 tokens each) + the new
     segment; per session 4 forward calls with fresh Q / K_new / V_new, then the
-    append of the new segment (rolled back after each session).  Inputs are
-    drawn on the device (timing only)."""
+    append of the new segment (rolled back after each session).  With `heads`
+    below 16 (one GPU's share when heads are sharded) the caches are small
+    enough to stay in the last-level cache, so `n_caches` identical caches
+    are rotated, one per call.  Inputs are drawn on the device (timing only)."""
     w = wl.long_session_720p()
-    H, D = w.heads, 128
+    H, D = heads or w.heads, 128
     g = torch.Generator(device="cuda")
     g.manual_seed(4000)
     rnd = lambda n: torch.randn((n, H, D), generator=g, device="cuda").to(torch.bfloat16)
     cap = w.n_cached + w.n_new
-    kb = torch.empty((H, cap, D), dtype=torch.bfloat16, device="cuda")
-    vb = torch.empty_like(kb)
-    cache = nm.nomas_kvcache_create(H, cap, kb, vb)
-    for s in w.cached:
-        nm.nomas_kvcache_append(cache, s, rnd(s.n_tokens), rnd(s.n_tokens))
+    caches = []
+    for _ in range(n_caches):
+        kb = torch.empty((H, cap, D), dtype=torch.bfloat16, device="cuda")
+        vb = torch.empty_like(kb)
+        c = nm.nomas_kvcache_create(H, cap, kb, vb)
+        for s in w.cached:
+            nm.nomas_kvcache_append(c, s, rnd(s.n_tokens), rnd(s.n_tokens))
+        caches.append(c)
+    cache = caches[0]
     t0 = time.perf_counter()
     plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H)
     plan_ms = (time.perf_counter() - t0) * 1e3
+    plans = [plan] + [nm.nomas_attn_plan(w.q_layout, w.new, c, heads=H) for c in caches[1:]]
     pinfo = plan.info()
     A = pinfo.unmasked_pairs
     qs = [rnd(w.n_q) for _ in range(4)]
@@ -184,12 +195,13 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record(stream)
         for n in range(4):
-            nm.nomas_attn_fwd(plan, cache, qs[n], ks[n], vs[n], o, lse, D ** -0.5, workspace=ws)
+            nm.nomas_attn_fwd(plans[n % n_caches], caches[n % n_caches], qs[n], ks[n], vs[n], o, lse,
+                              D ** -0.5, workspace=ws)
             ev[n + 1].record(stream)
         nm.nomas_kvcache_append(cache, w.new[0], ks[3], vs[3])
         ev[5].record(stream)
         torch.cuda.synchronize()
-        nm.nomas_kvcache_truncate(cache, n_seg)
+        nm.nomas_kvcache_truncate(cache, n_seg)   # back to the contents plans[0] was built on
         if it >= warmup:
             call_ms += [ev[n].elapsed_time(ev[n + 1]) for n in range(4)]
             app_ms.append(ev[4].elapsed_time(ev[5]))
@@ -203,7 +215,8 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1):
             "fwd_tflops": round(4.0 * D * H * A / (c * 1e-3) / 1e12, 2),
             "kv_stream_gbs": round(kv_bytes / (c * 1e-3) / 1e9, 1),
             "append_ms": round(a, 4), "append_gbs": round(app_bytes / (a * 1e-3) / 1e9, 1),
-            "session_ms": round(float(np.mean(sess_ms)), 3), "sessions": sessions}
+            "session_ms": round(float(np.mean(sess_ms)), 3), "sessions": sessions,
+            "caches_rotated": n_caches}
 
 
 def main():
@@ -217,6 +230,8 @@ def main():
                     help="skip the extra forward + backward row on the 131072-token pack")
     ap.add_argument("--no-long-session", action="store_true",
                     help="skip the extra 720p long-session row")
+    ap.add_argument("--no-sp8-share", action="store_true",
+                    help="skip the extra rows at one GPU's share of 16 heads sharded over 8")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (untimed), as a known "
                          "quantity for calibrating HBM byte counters")
@@ -365,6 +380,17 @@ def main():
         line["long_session"] = bench_long_session(nm, wl, torch)
     if not args.no_training:
         line["training_pack"] = bench_training(nm, wl, torch)
+    if not args.no_sp8_share:
+        # one GPU's share when the 16 heads are sharded over 8 GPUs (2 heads at
+        # full sequence length): 58 query-tile units on 256 CUs, so every unit
+        # is split and merged; the four rotated caches exceed the 256 MB
+        # last-level cache, as the layers of a real loop would
+        share = {"heads": 2}
+        if not args.no_long_session:
+            share["long_session"] = bench_long_session(nm, wl, torch, heads=2, n_caches=4)
+        if not args.no_training:
+            share["training_pack"] = bench_training(nm, wl, torch, heads=2)
+        line["sp8_share"] = share
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

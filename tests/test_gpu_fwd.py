@@ -246,6 +246,33 @@ def test_long_session_720p_sampled_rows():
     assert torch.equal(got, dev(kn[stored_rows(w.new)]))
 
 
+def test_long_session_720p_two_heads_split_units():
+    """One GPU's share of the 720p session when 16 heads are sharded over 8
+    GPUs: 2 heads, 29 query-tile pairs each, i.e. 58 units on 256 persistent
+    workgroups, so every unit is cut into several pieces and merged."""
+    need_gpu()
+    w = wl.long_session_720p()
+    H = 2
+    say("720p long session at 2 heads: 58 units split over 256 workgroups")
+    kc, vc = w.cache_kv()
+    kc, vc = np.ascontiguousarray(kc[:, :H]), np.ascontiguousarray(vc[:, :H])
+    cache = new_cache(H, w.n_cached + w.n_new)
+    fill_cache(cache, w.cached, dev(kc), dev(vc))
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H)
+    q = np.ascontiguousarray(w.q(0)[:, :H])
+    kn = np.ascontiguousarray(w.k_new(0)[:, :H])
+    vn = np.ascontiguousarray(w.v_new(0)[:, :H])
+    o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), H)
+    g = np.random.default_rng(46)
+    rows = np.sort(np.concatenate([g.choice(w.n_q, 48, replace=False),
+                                   np.arange(w.n_q - 256, w.n_q, 29)]))
+    keys = w.cached + w.new
+    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+                              rows=rows)
+    check_o(host(o)[rows], o_ref, "720p, 2 heads")
+    check_lse(host(l)[:, rows], l_ref, "720p, 2 heads")
+
+
 def test_training_pack_131k_forward_sampled():
     need_gpu()
     w = wl.training_pack_131k()
