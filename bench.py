@@ -22,6 +22,8 @@ rows), then the append.
 training_pack (extra, not the headline) = forward and backward times on the
 131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
 (four products) and, beside it, the FlashAttention convention 10 D H A.
+long_session_window4 (extra) = the same session with a sliding window of 4
+segments (whole segments; older ones, heads included, are not visible).
 sp8_share (extra) = both rows again at 2 heads, one GPU's share when the 16
 heads are sharded over 8 GPUs.
 """
@@ -154,7 +156,7 @@ def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
             "iters": iters}
 
 
-def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches=1):
+def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches=1, window=0):
     """720p long session: 16 cached segments (7,232 tokens each) + the new
     segment; per session 4 forward calls with fresh Q / K_new / V_new, then the
     append of the new segment (rolled back after each session).  With `heads`
@@ -177,9 +179,10 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches
         caches.append(c)
     cache = caches[0]
     t0 = time.perf_counter()
-    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=H, window=window)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    plans = [plan] + [nm.nomas_attn_plan(w.q_layout, w.new, c, heads=H) for c in caches[1:]]
+    plans = [plan] + [nm.nomas_attn_plan(w.q_layout, w.new, c, heads=H, window=window)
+                      for c in caches[1:]]
     pinfo = plan.info()
     A = pinfo.unmasked_pairs
     qs = [rnd(w.n_q) for _ in range(4)]
@@ -208,15 +211,20 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches
             sess_ms.append(ev[0].elapsed_time(ev[5]))
     c, a = float(np.mean(call_ms)), float(np.mean(app_ms))
     app_bytes = 2 * 2 * w.n_new * H * D * 2
-    kv_bytes = 2 * pinfo.n_keys * H * D * 2   # keys the call reads: cached rows + new tokens
-    return {"workload": w.name, "queries": w.n_q, "keys": int(pinfo.n_keys), "heads": H,
+    # keys the call reads: every key tile some query tile sees (all cached rows
+    # and new tokens without a window)
+    read_tiles = int((nm.nomas_plan_export_classes(plan) != 0).any(axis=0).sum())
+    keys_read = min(read_tiles * 64, int(pinfo.n_keys))
+    kv_bytes = 2 * keys_read * H * D * 2
+    return {"workload": w.name, "queries": w.n_q, "keys": int(pinfo.n_keys), "keys_read": keys_read,
+            "heads": H,
             "unmasked_pairs": A, "plan_host_ms": round(plan_ms, 2),
             "fwd_ms_per_call": round(c, 3),
             "fwd_tflops": round(4.0 * D * H * A / (c * 1e-3) / 1e12, 2),
             "kv_stream_gbs": round(kv_bytes / (c * 1e-3) / 1e9, 1),
             "append_ms": round(a, 4), "append_gbs": round(app_bytes / (a * 1e-3) / 1e9, 1),
             "session_ms": round(float(np.mean(sess_ms)), 3), "sessions": sessions,
-            "caches_rotated": n_caches}
+            "caches_rotated": n_caches, "window_segments": window}
 
 
 def main():
@@ -378,6 +386,9 @@ def main():
     }
     if not args.no_long_session:
         line["long_session"] = bench_long_session(nm, wl, torch)
+        # the same session with a sliding window of 4 segments (the new one and
+        # the 3 most recent cached ones): cost bounded whatever the session length
+        line["long_session_window4"] = bench_long_session(nm, wl, torch, window=4)
     if not args.no_training:
         line["training_pack"] = bench_training(nm, wl, torch)
     if not args.no_sp8_share:

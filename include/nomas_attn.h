@@ -119,7 +119,15 @@ typedef struct {
   int32_t block_k;         /* 0 = 64; the kernels support 64              */
   int32_t text_query_mode; /* NOMAS_TEXT_QUERY_*                          */
   int32_t flags;           /* NOMAS_PLAN_*                                */
-  int32_t reserved0;       /* set to 0                                    */
+  int32_t window_segments; /* sliding window over segments: 0 = none; W >= 1:
+                              a query of segment index s sees keys of
+                              segment indices s - W + 1 .. s of its video
+                              only (older segments, their heads included,
+                              become invisible and their tiles EMPTY).  The
+                              pages list sliding-window attention among the
+                              single-GPU inference optimisations ("Summary
+                              (Overview)", Inference) without its unit; a
+                              whole-segment window is the reading taken.  */
   int32_t reserved1;       /* set to 0                                    */
 } nomas_plan_opts;
 

@@ -32,7 +32,7 @@ def _f64(x):
 
 
 def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
-            rows=None, heads=None, block=512):
+            rows=None, heads=None, block=512, window=0):
     """O [len(rows), Hs, D] and LSE [Hs, len(rows)] (natural log), fp64.
 
     rows: query indices to evaluate (default all); heads: head indices.
@@ -44,7 +44,7 @@ def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
     lse = np.full((len(heads), len(rows)), -np.inf)
     for r0 in range(0, len(rows), block):
         ridx = rows[r0:r0 + block]
-        m = visible_mask(tq.take(ridx), tk, mode)
+        m = visible_mask(tq.take(ridx), tk, mode, window)
         any_vis = m.any(axis=1)
         for hi, h in enumerate(heads):
             s = scale * (q[ridx, h, :] @ k[:, h, :].T)
@@ -59,7 +59,7 @@ def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
 
 
 def backward(q, k, v, d_o, tq: TokenAttrs, tk: TokenAttrs, scale: float,
-             mode="R", heads=None, q_rows=None, k_rows=None, block=512):
+             mode="R", heads=None, q_rows=None, k_rows=None, block=512, window=0):
     """dQ [len(q_rows), Hs, D], dK and dV [len(k_rows), Hs, D], fp64.
 
     Every query contributes to dK/dV; q_rows / k_rows only select which rows
@@ -81,7 +81,7 @@ def backward(q, k, v, d_o, tq: TokenAttrs, tk: TokenAttrs, scale: float,
     dv = np.zeros((len(k_rows), len(heads), q.shape[2]))
     for r0 in range(0, nq, block):
         ridx = np.arange(r0, min(nq, r0 + block))
-        m = visible_mask(tq.take(ridx), tk, mode)
+        m = visible_mask(tq.take(ridx), tk, mode, window)
         any_vis = m.any(axis=1)
         sel = want_q[ridx]
         for hi, h in enumerate(heads):

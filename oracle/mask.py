@@ -22,6 +22,11 @@ Rules, each restated from the pages:
       no text query sees a tail; mode H -- head queries also see every tail of
       their own segment.
   (7) Padding is never visible and sees nothing.
+  (8) Sliding window (optional) -- [Summary] Inference lists sliding-window
+      attention among the single-GPU optimisations without saying over what;
+      read as whole segments: with a window of W >= 1 segments a query of
+      segment j sees only segments j - W + 1 .. j of its video (older heads
+      included in what is dropped).  window = 0 means no window.
 """
 from __future__ import annotations
 
@@ -32,9 +37,9 @@ from .tokens import A, H, PAD, V, TokenAttrs
 MODES = ("R", "K", "H")
 
 
-def visible_mask(tq: TokenAttrs, tk: TokenAttrs, mode: str = "R") -> np.ndarray:
+def visible_mask(tq: TokenAttrs, tk: TokenAttrs, mode: str = "R", window: int = 0) -> np.ndarray:
     """Boolean M[q, k] for the given query and key tokens (vectorised)."""
-    assert mode in MODES
+    assert mode in MODES and window >= 0
     qv = tq.video[:, None]
     qs = tq.seg[:, None]
     kv = tk.video[None, :]
@@ -44,6 +49,8 @@ def visible_mask(tq: TokenAttrs, tk: TokenAttrs, mode: str = "R") -> np.ndarray:
 
     live = (qkind != PAD) & (kkind != PAD)                 # rule (7)
     earlier_or_same = (qv == kv) & (ks <= qs)              # rules (1), (2)
+    if window:
+        earlier_or_same &= qs - ks < window                # rule (8)
     video_or_head_key = (kkind == V) | (kkind == H)        # rule (3) + video
     same_segment = (qv == kv) & (qs == ks)                 # rule (4)
 
@@ -89,7 +96,7 @@ def _locate(segments, t):
     raise IndexError("token outside layout")
 
 
-def visible_pair(q_seg, q_role, q_detail, k_seg, k_role, k_detail, mode="R") -> bool:
+def visible_pair(q_seg, q_role, q_detail, k_seg, k_role, k_detail, mode="R", window=0) -> bool:
     """One (query, key) decision written as nested cases, for brute force."""
     if q_role == "pad" or k_role == "pad":
         return False
@@ -97,6 +104,8 @@ def visible_pair(q_seg, q_role, q_detail, k_seg, k_role, k_detail, mode="R") -> 
         return False                     # different videos of a pack
     if k_seg.index > q_seg.index:
         return False                     # future segment
+    if window and q_seg.index - k_seg.index >= window:
+        return False                     # outside the sliding window
     if k_role in ("video", "head"):
         return True
     # key is a tail token of action k_detail
@@ -111,7 +120,7 @@ def visible_pair(q_seg, q_role, q_detail, k_seg, k_role, k_detail, mode="R") -> 
     return mode == "H"
 
 
-def brute_force_mask(q_segments, k_segments, mode="R") -> np.ndarray:
+def brute_force_mask(q_segments, k_segments, mode="R", window=0) -> np.ndarray:
     """M from visible_pair over every pair: O(nq*nk) Python calls; tiny only."""
     nq = sum(s.n_frames * s.tokens_per_frame + s.n_head +
              sum(a[0] for a in s.actions) + s.n_pad for s in q_segments)
@@ -123,5 +132,5 @@ def brute_force_mask(q_segments, k_segments, mode="R") -> np.ndarray:
         qs, qr, qd = _locate(q_segments, i)
         for j in range(nk):
             ks, kr, kd = kloc[j]
-            m[i, j] = visible_pair(qs, qr, qd, ks, kr, kd, mode)
+            m[i, j] = visible_pair(qs, qr, qd, ks, kr, kd, mode, window)
     return m

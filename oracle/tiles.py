@@ -22,16 +22,16 @@ from .tokens import TokenAttrs
 EMPTY, FULL, PARTIAL = 0, 1, 2
 
 
-def unmasked_pairs(tq: TokenAttrs, tk: TokenAttrs, mode="R", block=256) -> int:
+def unmasked_pairs(tq: TokenAttrs, tk: TokenAttrs, mode="R", block=256, window=0) -> int:
     total = 0
     for r0 in range(0, len(tq), block):
         total += int(visible_mask(tq.take(np.arange(r0, min(len(tq), r0 + block))),
-                                  tk, mode).sum())
+                                  tk, mode, window).sum())
     return total
 
 
 def tile_classes(tq: TokenAttrs, tk: TokenAttrs, bq: int, bk: int, mode="R",
-                 q_tiles=None) -> np.ndarray:
+                 q_tiles=None, window=0) -> np.ndarray:
     """uint8 [n_q_tiles (or len(q_tiles)), n_k_tiles] of EMPTY/FULL/PARTIAL."""
     nq, nk = len(tq), len(tk)
     nqt = -(-nq // bq)
@@ -42,7 +42,7 @@ def tile_classes(tq: TokenAttrs, tk: TokenAttrs, bq: int, bk: int, mode="R",
     col_area = np.bincount(col_tile, minlength=nkt)
     for i in q_tiles:
         r = np.arange(i * bq, min(nq, (i + 1) * bq))
-        m = visible_mask(tq.take(r), tk, mode)
+        m = visible_mask(tq.take(r), tk, mode, window)
         counts = np.add.reduceat(m.sum(axis=0), np.arange(0, nk, bk)) if nk else np.zeros(0, int)
         area = col_area * len(r)
         cls = np.full(nkt, PARTIAL, np.uint8)

@@ -159,7 +159,8 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
     return NOMAS_ERR_INVALID_ARGUMENT;
   }
   if (opts.flags & ~int32_t(NOMAS_PLAN_HOST_ONLY)) { *err = "unknown plan flag"; return NOMAS_ERR_INVALID_ARGUMENT; }
-  if (opts.reserved0 || opts.reserved1) { *err = "reserved option fields must be 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
+  if (opts.reserved1) { *err = "reserved option fields must be 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
+  if (opts.window_segments < 0) { *err = "window_segments must be >= 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
   p.bq = opts.block_q ? opts.block_q : 128;
   p.bk = opts.block_k ? opts.block_k : 64;
   const bool host_only = opts.flags & NOMAS_PLAN_HOST_ONLY;
@@ -217,7 +218,18 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   int64_t pos = 0;
   for (const auto& s : q) {
     int32_t o = ord[{s.video, s.index}];
-    q_runs(s, o, first_of_video[s.video], p.mode, &pos, &qr);
+    // first visible ordinal: the video's first segment, or with a window of W
+    // segments the first segment whose index is at least s.index - W + 1
+    // (ordinals follow (video, index) order, so that is a lower bound)
+    int32_t lo = first_of_video[s.video];
+    if (opts.window_segments > 0) {
+      const int64_t first_index = int64_t(s.index) - opts.window_segments + 1;
+      if (first_index > INT32_MIN) {
+        auto it = ord.lower_bound(Ident{s.video, int32_t(first_index)});
+        lo = std::max(lo, it->second);  // never past s itself, which is in ord
+      }
+    }
+    q_runs(s, o, lo, p.mode, &pos, &qr);
   }
   p.nq = pos;
   pos = 0;

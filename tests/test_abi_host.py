@@ -191,3 +191,44 @@ def test_backward_entry_checks_on_host_plans():
                             fake, fake, fake, 0.1, fake, n.value, None)
     assert st == _lib.ERR_INVALID_ARGUMENT and "host-only" in nm.nomas_last_error()
     assert lib.nomas_attn_bwd_workspace_size(None, C.byref(n)) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_plan_window_matches_oracle_with_gaps():
+    """Sliding window: plan A and classes against the oracle, on layouts whose
+    key set skips segments (the window counts segment indices, not the
+    segments present)."""
+    g = np.random.default_rng(4242)
+    for trial in range(120):
+        segs = random_tiny_layout(g, n_videos=int(g.integers(1, 3)))
+        keys = [s for s in segs if g.random() < 0.75] or segs[-1:]
+        qsegs = [s for s in segs if g.random() < 0.6] or segs[:1]
+        keys = sorted({(s.video, s.index): s for s in keys + qsegs}.values(),
+                      key=lambda s: (s.video, s.index))
+        window = int(g.integers(1, 4))
+        mode = "RKH"[trial % 3]
+        bq, bk = int(g.integers(1, 7)), int(g.integers(1, 7))
+        p = nm.nomas_attn_plan(qsegs, keys, heads=1, mode=mode, host_only=True, block_q=bq,
+                               block_k=bk, window=window)
+        tq, tk = oracle.expand(qsegs), oracle.expand(keys)
+        np.testing.assert_array_equal(nm.nomas_plan_export_classes(p),
+                                      oracle.tile_classes(tq, tk, bq, bk, mode, window=window))
+        assert p.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk, mode, window=window)
+
+
+@pytest.mark.parametrize("window", [1, 2])
+def test_plan_window_cached_step_480p(window):
+    w = wl.cached_step_480p()
+    keys = w.cached + w.new
+    p = host_plan(w.q_layout, keys, heads=16)
+    pw = nm.nomas_attn_plan(w.q_layout, keys, heads=16, host_only=True, window=window)
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    cls = nm.nomas_plan_export_classes(pw)
+    np.testing.assert_array_equal(cls, oracle.tile_classes(tq, tk, 128, 64, window=window))
+    assert pw.info().unmasked_pairs == oracle.unmasked_pairs(tq, tk, window=window)
+    assert pw.info().unmasked_pairs < p.info().unmasked_pairs
+
+
+def test_plan_window_rejects_negative():
+    segs = wl.tiny_two_segments().q_layout
+    with pytest.raises(nm.NomasError):
+        nm.nomas_attn_plan(segs, segs, heads=1, host_only=True, window=-1)

@@ -48,7 +48,7 @@ def run_bwd(plan, q, k, v, o, d_o, lse, heads):
     return dq, dk, dv
 
 
-def full_case(segs, heads, seed, mode="R", check_heads=None, fp32=False):
+def full_case(segs, heads, seed, mode="R", check_heads=None, fp32=False, window=0):
     """Whole-tensor comparison on a dense (no cache) layout."""
     n = wl.layout_tokens(segs)
     q = wl.randn((n, heads, 128), seed + 1, bf16=not fp32)
@@ -56,16 +56,17 @@ def full_case(segs, heads, seed, mode="R", check_heads=None, fp32=False):
     v = wl.randn((n, heads, 128), seed + 3, bf16=not fp32)
     d_o = wl.randn((n, heads, 128), seed + 4, bf16=not fp32)
     qb, kb, vb, dob = (wl.round_to_bf16(x) for x in (q, k, v, d_o))
-    plan = nm.nomas_attn_plan(segs, segs, heads=heads, mode=mode)
+    plan = nm.nomas_attn_plan(segs, segs, heads=heads, mode=mode, window=window)
     qd, kd, vd, dod = dev(qb), dev(kb), dev(vb), dev(dob)
     o, lse = run_fwd(plan, None, qd, kd, vd, heads)
     dq, dk, dv = run_bwd(plan, qd, kd, vd, o, dod, lse, heads)
     tq = oracle.expand(segs)
     hs = list(range(heads)) if check_heads is None else list(check_heads)
-    o_ref, l_ref = oracle.forward(qb, kb, vb, tq, tq, SCALE, mode=mode, heads=hs)
+    o_ref, l_ref = oracle.forward(qb, kb, vb, tq, tq, SCALE, mode=mode, heads=hs, window=window)
     check_o(host(o)[:, hs], o_ref, "O")
     check_lse(host(lse)[hs], l_ref, "LSE")
-    dq_ref, dk_ref, dv_ref = oracle.backward(qb, kb, vb, dob, tq, tq, SCALE, mode=mode, heads=hs)
+    dq_ref, dk_ref, dv_ref = oracle.backward(qb, kb, vb, dob, tq, tq, SCALE, mode=mode, heads=hs,
+                                             window=window)
     check_grad(host(dq)[:, hs], dq_ref, "dQ")
     check_grad(host(dk)[:, hs], dk_ref, "dK")
     check_grad(host(dv)[:, hs], dv_ref, "dV")
@@ -92,6 +93,14 @@ def test_pack_backward_text_query_modes(mode):
     w = wl.small_pack(1)
     say(f"pack, mode {mode}, 2 heads")
     full_case(w.q_layout, 2, 8300, mode=mode)
+
+
+@pytest.mark.parametrize("window", [1, 2])
+def test_pack_backward_sliding_window(window):
+    need_gpu()
+    w = wl.small_pack(2)
+    say(f"pack, window of {window} segment(s), 2 heads, backward")
+    full_case(w.q_layout, 2, 8600 + window, window=window)
 
 
 def test_ragged_pack_backward():

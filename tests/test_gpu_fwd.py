@@ -27,9 +27,9 @@ def dense_case(w, mode="R", nfe=0):
     return plan, q, k, v, keys
 
 
-def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None):
+def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None, window=0):
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
-    return oracle.forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads)
+    return oracle.forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads, window=window)
 
 
 def test_tiny_two_segments_fp32_inputs():
@@ -271,6 +271,25 @@ def test_long_session_720p_two_heads_split_units():
                               rows=rows)
     check_o(host(o)[rows], o_ref, "720p, 2 heads")
     check_lse(host(l)[:, rows], l_ref, "720p, 2 heads")
+
+
+@pytest.mark.parametrize("window", [1, 2])
+def test_cached_step_480p_sliding_window(window):
+    """Sliding window over whole segments: the new segment sees only itself
+    (window 1) or itself and the last cached segment (window 2); the older
+    cached tiles are EMPTY and never loaded."""
+    need_gpu()
+    w = wl.cached_step_480p()
+    say(f"480p cached step, window of {window} segment(s)")
+    cache, kc, vc = build_cached(w)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16, window=window)
+    q, kn, vn = w.q(), w.k_new(), w.v_new()
+    o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
+    keys = w.cached + w.new
+    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+                              heads=[1, 14], window=window)
+    check_o(host(o)[:, [1, 14]], o_ref, f"window {window}")
+    check_lse(host(l)[[1, 14]], l_ref, f"window {window}")
 
 
 def test_training_pack_131k_forward_sampled():

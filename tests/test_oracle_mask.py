@@ -165,3 +165,86 @@ def test_tile_classes_from_definition_random():
                     want = 0 if not blk.any() else (1 if blk.all() else 2)
                     assert cls[i, j] == want
             assert cls.shape == (-(-n // bq), -(-n // bk))
+
+
+# ---- sliding window over whole segments ------------------------------------
+
+def test_window_tiny_hand_count():
+    """The two-segment layout of the hand-built fixture with a one-segment
+    window: each of segment 1's 48 rows loses exactly the 40 video and head
+    keys of segment 0 (rows 0-39 in the fixture's per-row table), so
+    A = 6080 - 48 * 40 = 4160 and segment 1 then sees itself as segment 0
+    does; a window of two segments changes nothing."""
+    w = wl.tiny_two_segments()
+    t = oracle.expand(w.q_layout)
+    assert oracle.unmasked_pairs(t, t, window=1) == 4160
+    assert oracle.unmasked_pairs(t, t, window=2) == 6080
+    m1 = oracle.visible_mask(t, t, window=1)
+    assert not m1[48:, :48].any() and not m1[:48, 48:].any()
+    np.testing.assert_array_equal(m1[48:, 48:], m1[:48, :48])
+
+
+def test_window_vectorised_equals_brute_force():
+    g = np.random.default_rng(321)
+    for trial in range(150):
+        segs = random_tiny_layout(g)
+        mode = MODES[trial % 3]
+        window = int(g.integers(1, 4))
+        t = oracle.expand(segs)
+        np.testing.assert_array_equal(oracle.visible_mask(t, t, mode, window),
+                                      oracle.brute_force_mask(segs, segs, mode, window))
+
+
+def closed_form_A_window(segs, window, mode="R"):
+    """closed_form_A with the video + head sum restricted to the `window`
+    most recent segments (s.index - window < r.index <= s.index); tails are
+    seen only inside their own segment, which every window keeps."""
+    total = 0
+    for s in segs:
+        vh = sum(r.n_frames * r.tokens_per_frame + r.n_head for r in segs
+                 if r.video == s.video and s.index - window < r.index <= s.index)
+        L = [a[0] for a in s.actions]
+        total += (s.n_frames * s.tokens_per_frame + s.n_head + sum(L)) * vh
+        for (ln, lo, hi) in s.actions:
+            total += ln * s.tokens_per_frame * (hi - lo) + (ln * ln if mode in ("R", "H") else 0)
+        if mode == "H":
+            total += s.n_head * sum(L)
+    return total
+
+
+def test_closed_form_A_window_random():
+    g = np.random.default_rng(77)
+    for trial in range(80):
+        segs = random_tiny_layout(g)
+        t = oracle.expand(segs)
+        for window in (1, 2, 3):
+            for mode in MODES:
+                assert oracle.unmasked_pairs(t, t, mode, window=window) == \
+                    closed_form_A_window(segs, window, mode)
+
+
+def test_window_one_is_block_diagonal_over_segments():
+    """With a one-segment window every segment attends to itself alone: the
+    mask is block-diagonal, each block the unwindowed mask of that segment
+    taken on its own."""
+    g = np.random.default_rng(8)
+    for _ in range(30):
+        segs = random_tiny_layout(g)
+        t = oracle.expand(segs)
+        sizes = [len(oracle.expand([s])) for s in segs]
+        want = np.zeros((len(t), len(t)), bool)
+        o = 0
+        for s, n in zip(segs, sizes):
+            ts = oracle.expand([s])
+            want[o:o + n, o:o + n] = oracle.visible_mask(ts, ts)
+            o += n
+        np.testing.assert_array_equal(oracle.visible_mask(t, t, window=1), want)
+
+
+def test_window_covering_every_segment_is_no_window():
+    g = np.random.default_rng(9)
+    for _ in range(30):
+        segs = random_tiny_layout(g)
+        t = oracle.expand(segs)
+        w = 1 + max(s.index for s in segs)
+        np.testing.assert_array_equal(oracle.visible_mask(t, t, window=w), oracle.visible_mask(t, t))
