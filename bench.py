@@ -22,6 +22,8 @@ rows), then the append.
 training_pack (extra, not the headline) = forward and backward times on the
 131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
 (four products) and, beside it, the FlashAttention convention 10 D H A.
+sparse_step (extra) = the 480p step with its last two denoising calls keeping
+25% of the video key tiles (video-block sparsity) and the first two dense.
 long_session_window4 (extra) = the same session with a sliding window of 4
 segments (whole segments; older ones, heads included, are not visible).
 sp8_share (extra) = both rows again at 2 heads, one GPU's share when the 16
@@ -238,6 +240,8 @@ def main():
                     help="skip the extra forward + backward row on the 131072-token pack")
     ap.add_argument("--no-long-session", action="store_true",
                     help="skip the extra 720p long-session row")
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the extra 480p step whose last two denoising calls are sparse")
     ap.add_argument("--no-sp8-share", action="store_true",
                     help="skip the extra rows at one GPU's share of 16 heads sharded over 8")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -291,14 +295,25 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
     n_cached_segs = len(w.cached)
 
-    def step(fwd_events=None, app_events=None):
+    # video-block sparse plans for the last two denoising calls (extra row)
+    KEEP = 25
+    sp_plans = [] if args.no_sparse else \
+        [nm.nomas_attn_plan(w.q_layout, w.new, c, heads=H, video_keep_percent=KEEP) for c in caches]
+    ws_sparse = torch.empty(max(nm.nomas_attn_fwd_workspace_size(sp_plans[0]), 16), dtype=torch.uint8,
+                            device="cuda") if sp_plans else None
+
+    def step(fwd_events=None, app_events=None, sparse=False):
         for n in range(NFE):
             for layer in range(L):
                 if fwd_events is not None:
                     e0, e1 = ev(), ev()
                     e0.record(stream)
-                nm.nomas_attn_fwd(plans[layer], caches[layer], qs[n], ks[n], vs[n], outs[layer],
-                                  lses[layer], D ** -0.5, workspace=ws)
+                if sparse and n >= 2:
+                    nm.nomas_attn_fwd(sp_plans[layer], caches[layer], qs[n], ks[n], vs[n], outs[layer],
+                                      lses[layer], D ** -0.5, workspace=ws_sparse)
+                else:
+                    nm.nomas_attn_fwd(plans[layer], caches[layer], qs[n], ks[n], vs[n], outs[layer],
+                                      lses[layer], D ** -0.5, workspace=ws)
                 if fwd_events is not None:
                     e1.record(stream)
                     fwd_events.append((e0, e1))
@@ -343,6 +358,34 @@ def main():
     for _ in range(args.steps):
         step(fwd_ev, app_ev)
     torch.cuda.synchronize()
+
+    # extra: the step with the last two denoising calls video-block sparse
+    sparse_row = None
+    if sp_plans:
+        for _ in range(args.warmup):
+            step(sparse=True)
+        s0, s1 = ev(), ev()
+        torch.cuda.synchronize()
+        s0.record(stream)
+        for _ in range(args.steps):
+            step(sparse=True)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        ms_sparse_step = s0.elapsed_time(s1) / args.steps
+        sp_ev = []
+        for _ in range(args.steps):
+            step(sp_ev, sparse=True)
+        torch.cuda.synchronize()
+        per_call = [a.elapsed_time(b) for a, b in sp_ev]
+        sparse_calls = [t for i, t in enumerate(per_call) if (i // L) % NFE >= 2]
+        dense_entries = nm.nomas_attn_plan(w.q_layout, w.new, caches[0], heads=H, host_only=True,
+                                           video_keep_percent=100).info().sparse_list_entries
+        kept = sp_plans[0].info().sparse_list_entries
+        sparse_row = {"video_keep_percent": KEEP, "dense_calls": 2, "sparse_calls": 2,
+                      "step_ms": round(ms_sparse_step, 4),
+                      "speedup_vs_dense_step": round(ms_step / ms_sparse_step, 3),
+                      "sparse_fwd_ms_per_call": round(float(np.mean(sparse_calls)), 4),
+                      "kept_tile_fraction": round(kept / dense_entries, 4)}
     fwd_ms = np.array([a.elapsed_time(b) for a, b in fwd_ev])
     app_ms = np.array([a.elapsed_time(b) for a, b in app_ev])
 
@@ -384,6 +427,8 @@ def main():
         "plan_host_ms": round(plan_ms, 3),
         "kernel_sha": kernel_hash(),
     }
+    if sparse_row is not None:
+        line["sparse_step"] = sparse_row
     if not args.no_long_session:
         line["long_session"] = bench_long_session(nm, wl, torch)
         # the same session with a sliding window of 4 segments (the new one and

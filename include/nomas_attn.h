@@ -128,7 +128,24 @@ typedef struct {
                               single-GPU inference optimisations ("Summary
                               (Overview)", Inference) without its unit; a
                               whole-segment window is the reading taken.  */
-  int32_t reserved1;       /* set to 0                                    */
+  int32_t video_keep_percent; /* video-block sparsity: 0 = dense; P in
+                              1..100: in every (head, query-tile pair) unit
+                              only ceil(P% of its video key tiles) are
+                              attended -- those with the highest block score
+                              (below) -- while key tiles holding any head,
+                              tail or padding token are always kept.  The
+                              pages keep 25% of video blocks after the first
+                              two denoising steps ("Summary (Overview)",
+                              Inference) without stating the selection; the
+                              score taken is, in fp32, the dot product of the
+                              unit's query sum and the tile's key sum:
+                              s = sum_d (sum_q Q[q,d]) * (sum_k K[k,d]),
+                              with separately rounded adds and products; a
+                              row sum adds groups of 16 consecutive rows
+                              (each in ascending order) in ascending group
+                              order, from +0.0; the dot runs over ascending
+                              d; ties go to the lower key tile.  Forward
+                              only.                                        */
 } nomas_plan_opts;
 
 typedef struct nomas_plan nomas_plan;
@@ -153,6 +170,10 @@ typedef struct {
   int32_t block_k;
   int32_t num_heads;
   int32_t text_query_mode;
+  int64_t sparse_list_entries; /* per head: key tiles the units of a sparse
+                                  plan attend (sum over units); 0 if dense */
+  int32_t video_keep_percent;
+  int32_t window_segments;
 } nomas_plan_info;
 
 /* --------------------------------------------------------------------------

@@ -37,6 +37,9 @@ choice, never hidden):
     visible.
   * token order in a segment: [video frame-major | head | a_0 | ... | pad].
   * rows with no visible key (padding) give O = 0 and LSE = -inf.
+  * sliding window (optional, mask.py rule 8): whole segments.
+  * video-block sparsity (optional, sparse.py): which blocks are kept is
+    stated there (pooled-sum block score in fp32, ties to the lower tile).
 
 Parity status: every function here is pinned by CPU tests (hand-built masks,
 closed forms, library special cases, finite differences, brute force) except
@@ -47,3 +50,4 @@ from .tokens import TokenAttrs, expand, V, H, A, PAD  # noqa: F401
 from .mask import visible_mask, visible_pair, brute_force_mask  # noqa: F401
 from .attention import forward, backward  # noqa: F401
 from .tiles import unmasked_pairs, tile_classes, EMPTY, FULL, PARTIAL  # noqa: F401
+from . import sparse  # noqa: F401

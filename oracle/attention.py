@@ -32,10 +32,12 @@ def _f64(x):
 
 
 def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
-            rows=None, heads=None, block=512, window=0):
+            rows=None, heads=None, block=512, window=0, tile_keep=None):
     """O [len(rows), Hs, D] and LSE [Hs, len(rows)] (natural log), fp64.
 
     rows: query indices to evaluate (default all); heads: head indices.
+    tile_keep: optional bool [H, query pairs, key tiles] (sparse.select_tiles):
+    key tile t is hidden from the queries of pair u in head h where False.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
@@ -44,9 +46,11 @@ def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
     lse = np.full((len(heads), len(rows)), -np.inf)
     for r0 in range(0, len(rows), block):
         ridx = rows[r0:r0 + block]
-        m = visible_mask(tq.take(ridx), tk, mode, window)
-        any_vis = m.any(axis=1)
+        m0 = visible_mask(tq.take(ridx), tk, mode, window)
         for hi, h in enumerate(heads):
+            m = m0 if tile_keep is None else \
+                m0 & tile_keep[h][ridx // 256][:, np.arange(k.shape[0]) // 64]
+            any_vis = m.any(axis=1)
             s = scale * (q[ridx, h, :] @ k[:, h, :].T)
             s = np.where(m, s, -np.inf)
             mx = np.where(any_vis, s.max(axis=1), 0.0)

@@ -43,7 +43,7 @@ class nomas_layout(C.Structure):
 class nomas_plan_opts(C.Structure):
     _fields_ = [("num_heads", C.c_int32), ("head_dim", C.c_int32), ("block_q", C.c_int32),
                 ("block_k", C.c_int32), ("text_query_mode", C.c_int32), ("flags", C.c_int32),
-                ("window_segments", C.c_int32), ("reserved1", C.c_int32)]
+                ("window_segments", C.c_int32), ("video_keep_percent", C.c_int32)]
 
 
 class nomas_plan_info(C.Structure):
@@ -53,7 +53,8 @@ class nomas_plan_info(C.Structure):
                 ("n_partial_tiles", C.c_int64), ("unmasked_pairs", C.c_int64),
                 ("executed_pairs", C.c_int64), ("effective_flop", C.c_double),
                 ("block_q", C.c_int32), ("block_k", C.c_int32), ("num_heads", C.c_int32),
-                ("text_query_mode", C.c_int32)]
+                ("text_query_mode", C.c_int32), ("sparse_list_entries", C.c_int64),
+                ("video_keep_percent", C.c_int32), ("window_segments", C.c_int32)]
 
 
 class NomasError(RuntimeError):
@@ -203,11 +204,11 @@ class KVCache:
 # ----------------------------------------------------------------------------
 
 def nomas_attn_plan(q_layout, kv_layout, cache=None, *, heads=16, mode="R", host_only=False,
-                    block_q=0, block_k=0, window=0) -> Plan:
+                    block_q=0, block_k=0, window=0, video_keep_percent=0) -> Plan:
     lib = load()
     ql, kl = _Layout(q_layout), _Layout(kv_layout)
     opts = nomas_plan_opts(heads, HEAD_DIM, block_q, block_k, TEXT_QUERY[mode],
-                           PLAN_HOST_ONLY if host_only else 0, window, 0)
+                           PLAN_HOST_ONLY if host_only else 0, window, video_keep_percent)
     out = C.c_void_p()
     _check(lib.nomas_attn_plan(C.byref(ql.c), C.byref(kl.c),
                                cache.handle if cache is not None else None,

@@ -26,6 +26,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU forms are kept out of the device code on purpose.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-ffp-contract=fast", "-munsafe-fp-atomics"]
+# Per-file additions (later flags win): the video-block score is defined with
+# separately rounded products and adds, so nothing in that file is fused.
+DEVICE_EXTRA = {"select.hip": ["-ffp-contract=off"]}
 
 
 def _run(cmd):
@@ -46,7 +49,7 @@ def build(verbose: bool = False) -> str:
         src = os.path.join(CSRC, f)
         obj = os.path.join(BUILD, f + ".o")
         if f.endswith(".hip"):
-            cmd = [HIPCC, *COMMON, *DEVICE, "-c", src, "-o", obj]
+            cmd = [HIPCC, *COMMON, *DEVICE, *DEVICE_EXTRA.get(f, []), "-c", src, "-o", obj]
         else:
             cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", src, "-o", obj]
         jobs.append((cmd, obj))

@@ -66,6 +66,7 @@ struct nomas_plan {
   const int32_t *d_pair_ptr = nullptr, *d_pair_idx = nullptr;
   const int32_t *d_kpair_ptr = nullptr, *d_kpair_idx = nullptr;
   const int32_t* d_unit_shift = nullptr;
+  const int32_t *d_sp_ptr = nullptr, *d_sp_keep = nullptr, *d_video_tile = nullptr;
 };
 
 namespace {
@@ -185,6 +186,14 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     groups = cus * nomas::attn_fwd_groups_per_cu();
   }
   nomas::build_fwd_schedule(&p->host, groups);
+  if (p->host.keep_percent > 0) {
+    for (int64_t u = 0; u < p->host.n_pairs; ++u)
+      if (p->host.pair_ptr[size_t(u + 1)] - p->host.pair_ptr[size_t(u)] > nomas::SELECT_MAX_ENTRIES) {
+        delete p;
+        return fail(NOMAS_ERR_UNSUPPORTED, "video_keep_percent: a query-tile pair sees more than " +
+                                               std::to_string(nomas::SELECT_MAX_ENTRIES) + " key tiles");
+      }
+  }
   if (!p->has_cache) nomas::build_bwd_schedule(&p->host);
   if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
     const nomas::HostPlan& h = p->host;
@@ -202,7 +211,10 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
                     {h.pair_idx.data(), h.pair_idx.size() * 4, 0},
                     {h.kpair_ptr.data(), h.kpair_ptr.size() * 4, 0},
                     {h.kpair_idx.data(), h.kpair_idx.size() * 4, 0},
-                    {h.unit_shift.data(), h.unit_shift.size() * 4, 0}};
+                    {h.unit_shift.data(), h.unit_shift.size() * 4, 0},
+                    {h.sp_ptr.data(), h.sp_ptr.size() * 4, 0},
+                    {h.sp_keep.data(), h.sp_keep.size() * 4, 0},
+                    {h.video_tile.data(), h.video_tile.size() * 4, 0}};
     size_t total = 0;
     for (Part& part : parts) {
       part.off = total;
@@ -237,6 +249,9 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->d_kpair_ptr = reinterpret_cast<const int32_t*>(base + parts[11].off);
     p->d_kpair_idx = reinterpret_cast<const int32_t*>(base + parts[12].off);
     p->d_unit_shift = reinterpret_cast<const int32_t*>(base + parts[13].off);
+    p->d_sp_ptr = reinterpret_cast<const int32_t*>(base + parts[14].off);
+    p->d_sp_keep = reinterpret_cast<const int32_t*>(base + parts[15].off);
+    p->d_video_tile = reinterpret_cast<const int32_t*>(base + parts[16].off);
     p->on_device = true;
   }
   *out = p;
@@ -261,6 +276,9 @@ nomas_status nomas_plan_get_info(const nomas_plan* p, nomas_plan_info* info) {
   info->block_k = h.bk;
   info->num_heads = h.heads;
   info->text_query_mode = h.mode;
+  info->sparse_list_entries = h.sp_total;
+  info->video_keep_percent = h.keep_percent;
+  info->window_segments = h.window;
   return ok();
 }
 
@@ -282,9 +300,34 @@ nomas_status nomas_plan_destroy(nomas_plan* p) {
 // forward
 // ---------------------------------------------------------------------------
 
+// Forward workspace: [sparse plans: kept lists [H][sp_total] int32 | key sums
+// [H][nkt][128] fp32 | query sums [H][n_pairs][128] fp32] [partial slots],
+// each part 256-byte aligned.
+struct FwdWorkspace {
+  size_t lists = 0, k_sum = 0, q_sum = 0, partial = 0, total = 0;
+};
+
+FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
+  auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
+  FwdWorkspace w;
+  size_t at = 0;
+  if (h.keep_percent > 0) {
+    w.lists = at;
+    at += al(size_t(h.heads) * size_t(h.sp_total) * 4);
+    w.k_sum = at;
+    at += al(size_t(h.heads) * size_t(h.nkt) * 128 * 4);
+    w.q_sum = at;
+    at += al(size_t(h.heads) * size_t(h.n_pairs) * 128 * 4);
+  }
+  w.partial = at;
+  at += (size_t)h.n_slots * nomas::attn_fwd_slot_bytes();
+  w.total = at;
+  return w;
+}
+
 nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  *bytes = (size_t)p->host.n_slots * nomas::attn_fwd_slot_bytes();
+  *bytes = fwd_workspace(p->host).total;
   return ok();
 }
 
@@ -310,11 +353,39 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
     return s;
   if (has_new && (s = check_stride(kv_stride, h.heads, "kv"))) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-  size_t need = (size_t)h.n_slots * nomas::attn_fwd_slot_bytes();
+  const FwdWorkspace ws = fwd_workspace(h);
+  size_t need = ws.total;
   if (need && (!workspace || workspace_bytes < need))
     return fail(NOMAS_ERR_INVALID_ARGUMENT, "workspace missing or smaller than nomas_attn_fwd_workspace_size");
   if ((s = check_dev_ptr(workspace, need > 0, "workspace"))) return s;
   if ((s = check_device(p))) return s;
+  char* wsb = static_cast<char*>(workspace);
+  if (h.keep_percent > 0 && h.nq > 0) {
+    nomas::SelParams sp{};
+    sp.q = static_cast<const uint16_t*>(q);
+    sp.k_cache = cache ? static_cast<const uint16_t*>(cache->k) : nullptr;
+    sp.k_new = static_cast<const uint16_t*>(k_new);
+    sp.pair_ptr = p->d_pair_ptr;
+    sp.pair_idx = p->d_pair_idx;
+    sp.sp_ptr = p->d_sp_ptr;
+    sp.sp_keep = p->d_sp_keep;
+    sp.video_tile = p->d_video_tile;
+    sp.k_sum = reinterpret_cast<float*>(wsb + ws.k_sum);
+    sp.q_sum = reinterpret_cast<float*>(wsb + ws.q_sum);
+    sp.lists = reinterpret_cast<int32_t*>(wsb + ws.lists);
+    sp.q_stride = q_stride;
+    sp.kv_stride = kv_stride;
+    sp.cache_cap = cache ? cache->capacity : 0;
+    sp.sp_total = h.sp_total;
+    sp.nq = (int32_t)h.nq;
+    sp.nk = (int32_t)h.nk;
+    sp.n_cached = (int32_t)h.n_cached;
+    sp.heads = h.heads;
+    sp.nkt = (int32_t)h.nkt;
+    sp.n_pairs = (int32_t)h.n_pairs;
+    hipError_t e = nomas::launch_select(sp, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "video-block selection launch");
+  }
 
   nomas::FwdParams fp{};
   fp.q = static_cast<const uint16_t*>(q);
@@ -326,14 +397,21 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
   fp.lse = lse;
   fp.qdesc = p->d_qdesc;
   fp.kdesc = p->d_kdesc;
-  fp.csr_ptr = p->d_pair_ptr;
-  fp.csr_idx = p->d_pair_idx;
+  if (h.keep_percent > 0) {  // per-head lists chosen by the selection above
+    fp.csr_ptr = p->d_sp_ptr;
+    fp.csr_idx = reinterpret_cast<const int32_t*>(wsb + ws.lists);
+    fp.list_head_stride = h.sp_total;
+  } else {
+    fp.csr_ptr = p->d_pair_ptr;
+    fp.csr_idx = p->d_pair_idx;
+    fp.list_head_stride = 0;
+  }
   fp.n_pairs = (int32_t)h.n_pairs;
   fp.wg_ptr = p->d_wg_ptr;
   fp.pieces = p->d_pieces;
   fp.combine = p->d_combine;
   fp.unit_shift = p->d_unit_shift;
-  fp.partial = static_cast<float*>(workspace);
+  fp.partial = reinterpret_cast<float*>(wsb + ws.partial);
   fp.groups = h.fwd_groups;
   fp.n_combine = (int32_t)h.combine.size();
   fp.q_stride = q_stride;
@@ -370,6 +448,7 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!p->on_device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "host-only plan cannot run");
   if (p->has_cache) return fail(NOMAS_ERR_INVALID_ARGUMENT, "backward needs a plan without a cache");
+  if (p->host.keep_percent > 0) return fail(NOMAS_ERR_UNSUPPORTED, "backward of a video-block sparse plan");
   const nomas::HostPlan& h = p->host;
   const bool hq = h.nq > 0, hk = h.nk > 0;
   nomas_status s;

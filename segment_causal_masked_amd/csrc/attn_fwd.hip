@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int qrow = pr * UNIT_ROWS + w * 32 + jq;
     // entries in the unit's rotated order: tile t of this piece is list entry
     // (e_begin + t + shift) mod n_unit
-    const const_i32p ulist = unit_idx + unit_ptr[pr];
+    const const_i32p ulist = unit_idx + p.list_head_stride * h + unit_ptr[pr];
     const int n_unit = unit_ptr[pr + 1] - unit_ptr[pr];
     const int rot = e_begin + ((const_i32p)p.unit_shift)[unit];
     auto ent_at = [&](int t) {

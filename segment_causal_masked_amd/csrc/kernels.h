@@ -32,6 +32,8 @@ struct FwdParams {
   const int4* pieces;      // {unit, entry_begin, entry_end, slot or -1}
   const int4* combine;     // {unit, first_slot, n_pieces, 0}
   const int32_t* unit_shift;  // per unit: entries visited in order (j + shift) mod n
+  int64_t list_head_stride;    // lists per head (sparse plans), else 0: unit (h, u')
+                               // walks csr_idx + h * list_head_stride + csr_ptr[u']
   float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
   int64_t q_stride, kv_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;
@@ -40,6 +42,26 @@ struct FwdParams {
 };
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
+
+// Video-block selection of sparse plans (select.hip): per (head, query-tile
+// pair) the kept key-tile list, written to `lists`.
+struct SelParams {
+  const uint16_t* q;        // [nq][H][128] bf16, stride q_stride
+  const uint16_t* k_cache;  // [H][cap][128] bf16 (or null)
+  const uint16_t* k_new;    // [n_new][H][128] bf16, stride kv_stride
+  const int32_t* pair_ptr;  // dense merged lists per pair (n_pairs + 1)
+  const int32_t* pair_idx;  // (k_tile << 4) | flags
+  const int32_t* sp_ptr;    // sparse list prefix per pair (n_pairs + 1)
+  const int32_t* sp_keep;   // video entries kept per pair
+  const int32_t* video_tile;  // per key tile: 1 = every key a video token
+  float* k_sum;             // workspace [H][nkt][128]
+  float* q_sum;             // workspace [H][n_pairs][128]
+  int32_t* lists;           // workspace [H][sp_total]
+  int64_t q_stride, kv_stride, cache_cap, sp_total;
+  int32_t nq, nk, n_cached, heads, nkt, n_pairs;
+};
+constexpr int SELECT_MAX_ENTRIES = 4096;  // longest pair list a sparse plan may have
+hipError_t launch_select(const SelParams& p, hipStream_t stream);
 size_t attn_fwd_slot_bytes();
 int attn_fwd_groups_per_cu();  // persistent forward workgroups per CU
 

@@ -159,8 +159,13 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
     return NOMAS_ERR_INVALID_ARGUMENT;
   }
   if (opts.flags & ~int32_t(NOMAS_PLAN_HOST_ONLY)) { *err = "unknown plan flag"; return NOMAS_ERR_INVALID_ARGUMENT; }
-  if (opts.reserved1) { *err = "reserved option fields must be 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
   if (opts.window_segments < 0) { *err = "window_segments must be >= 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
+  if (opts.video_keep_percent < 0 || opts.video_keep_percent > 100) {
+    *err = "video_keep_percent must be in [0, 100]";
+    return NOMAS_ERR_INVALID_ARGUMENT;
+  }
+  p.keep_percent = opts.video_keep_percent;
+  p.window = opts.window_segments;
   p.bq = opts.block_q ? opts.block_q : 128;
   p.bk = opts.block_k ? opts.block_k : 64;
   const bool host_only = opts.flags & NOMAS_PLAN_HOST_ONLY;
@@ -253,6 +258,30 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   for (const Run& r : kr)
     std::fill(p.kdesc.begin() + r.start, p.kdesc.begin() + r.start + r.len, kd_of(r));
 
+  // ---- video key tiles (every key a video token) ----------------------------
+  {
+    std::vector<uint8_t> is_video(size_t(p.nk), 0);
+    int64_t at = 0;
+    auto mark = [&](const nomas_segment& s, bool cached) {
+      const int64_t nv = int64_t(s.n_frames) * s.tokens_per_frame;
+      std::fill(is_video.begin() + at, is_video.begin() + at + nv, uint8_t(1));
+      int64_t rest = s.n_head;
+      if (!cached) {
+        for (int a = 0; a < s.n_actions; ++a) rest += s.actions[a].n_tokens;
+        rest += s.n_pad;
+      }
+      at += nv + rest;
+    };
+    for (const auto& s : cached) mark(s, true);
+    for (const auto& s : kv_new) mark(s, false);
+    p.video_tile.assign(size_t(p.nkt), 0);
+    for (int64_t j = 0; j < p.nkt; ++j) {
+      const int64_t a = j * p.bk, e = std::min(p.nk, a + p.bk);
+      p.video_tile[size_t(j)] = std::all_of(is_video.begin() + a, is_video.begin() + e,
+                                            [](uint8_t v) { return v != 0; });
+    }
+  }
+
   // ---- A = visible pairs, from run pairs -------------------------------------
   int64_t A = 0;
   for (const Run& a : qr)
@@ -330,8 +359,29 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     p.pair_ptr[size_t(u + 1)] = int32_t(p.pair_idx.size());
   }
 
+  // sparse lists: per pair, non-video entries + ceil(keep% of the video ones)
+  p.sp_ptr.clear();
+  p.sp_keep.clear();
+  p.sp_total = 0;
+  if (p.keep_percent > 0) {
+    p.sp_ptr.assign(size_t(p.n_pairs + 1), 0);
+    p.sp_keep.assign(size_t(p.n_pairs), 0);
+    for (int64_t u = 0; u < p.n_pairs; ++u) {
+      int32_t nv = 0;
+      for (int32_t e = p.pair_ptr[size_t(u)]; e < p.pair_ptr[size_t(u + 1)]; ++e)
+        nv += p.video_tile[size_t(p.pair_idx[size_t(e)] >> 4)];
+      const int32_t n = p.pair_ptr[size_t(u + 1)] - p.pair_ptr[size_t(u)];
+      const int32_t keep = int32_t((int64_t(nv) * p.keep_percent + 99) / 100);
+      p.sp_keep[size_t(u)] = keep;
+      p.sp_ptr[size_t(u + 1)] = p.sp_ptr[size_t(u)] + (n - nv) + keep;
+    }
+    p.sp_total = p.sp_ptr.back();
+  }
+  // the lists the forward walks: the merged pair lists, or the sparse ones
+  const std::vector<int32_t>& lptr = p.keep_percent > 0 ? p.sp_ptr : p.pair_ptr;
+
   const int64_t n_units = int64_t(p.heads) * p.n_pairs;
-  const int64_t row_total = p.pair_ptr.back();
+  const int64_t row_total = lptr.back();
   const int64_t total = int64_t(p.heads) * row_total;
   groups = std::max<int32_t>(1, groups);
   p.fwd_groups = groups;
@@ -348,8 +398,8 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   };
   for (int64_t u = 0; u < n_units; ++u) {
     const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
-    const int64_t n = p.pair_ptr[size_t(pr + 1)] - p.pair_ptr[size_t(pr)];
-    const int64_t start = h * row_total + p.pair_ptr[size_t(pr)];
+    const int64_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
+    const int64_t start = h * row_total + lptr[size_t(pr)];
     if (n == 0) {  // nothing visible: still owes zeros / -inf to its rows
       per[size_t(group_of(std::min(start, std::max<int64_t>(total - 1, 0))))].push_back(
           Piece{int32_t(u), 0, 0, -1});
@@ -380,9 +430,9 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   p.unit_shift.assign(size_t(n_units), 0);
   for (int64_t u = 0; u < n_units; ++u) {
     const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
-    const int64_t n = p.pair_ptr[size_t(pr + 1)] - p.pair_ptr[size_t(pr)];
+    const int64_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
     if (n == 0) continue;
-    const int64_t start = h * row_total + p.pair_ptr[size_t(pr)];
+    const int64_t start = h * row_total + lptr[size_t(pr)];
     const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
     int64_t best_g = g0, best_len = -1;
     for (int64_t g = g0; g <= g1; ++g) {

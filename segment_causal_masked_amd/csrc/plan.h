@@ -76,6 +76,14 @@ struct HostPlan {
   // per unit: its entries are visited in the rotated order
   // (j + unit_shift) mod n for j = 0 .. n - 1; pieces are ranges of j
   std::vector<int32_t> unit_shift;
+  // video-block sparsity (keep_percent > 0): per key tile, 1 if every key in
+  // it is a video token; per pair, the prefix of its sparse list lengths
+  // (non-video entries + ceil(keep_percent% of its video entries)); the
+  // lists themselves are chosen on the device per head.
+  int32_t keep_percent = 0, window = 0;
+  std::vector<int32_t> video_tile;
+  std::vector<int32_t> sp_ptr, sp_keep;
+  int64_t sp_total = 0;
   // backward schedule (build_bwd_schedule): per pair of key tiles (2 u,
   // 2 u + 1) the union of their non-empty q-tiles, entry = (q_tile << 4) |
   // flags with bit 0 / 1 = mask for the first / second key tile (PARTIAL,

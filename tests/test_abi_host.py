@@ -232,3 +232,33 @@ def test_plan_window_rejects_negative():
     segs = wl.tiny_two_segments().q_layout
     with pytest.raises(nm.NomasError):
         nm.nomas_attn_plan(segs, segs, heads=1, host_only=True, window=-1)
+
+
+@pytest.mark.parametrize("keep", [1, 25, 60, 100])
+def test_plan_sparse_list_lengths_match_oracle(keep):
+    """The plan sizes each (head, pair) list as its text tiles plus
+    ceil(keep% of its video tiles); the oracle's selection kept exactly that."""
+    from oracle import sparse
+    w = wl.cached_step_480p()
+    keys = w.cached + w.new
+    p = nm.nomas_attn_plan(w.q_layout, keys, heads=16, host_only=True, video_keep_percent=keep)
+    info = p.info()
+    assert info.video_keep_percent == keep
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    q = w.q()[:, :1]
+    kc, _ = w.cache_kv()
+    k = np.concatenate([kc, w.k_new()])[:, :1]
+    kept = sparse.select_tiles(q, k, tq, tk, keep)
+    cls = oracle.tile_classes(tq, tk, 128, 64)
+    total = 0
+    for u in range(kept.shape[1]):
+        seen = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
+        total += int((kept[0, u] & seen).sum())
+    assert info.sparse_list_entries == total
+
+
+def test_plan_sparse_rejects_out_of_range():
+    segs = wl.tiny_two_segments().q_layout
+    for bad in (-1, 101):
+        with pytest.raises(nm.NomasError):
+            nm.nomas_attn_plan(segs, segs, heads=1, host_only=True, video_keep_percent=bad)
