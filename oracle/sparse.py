@@ -82,7 +82,7 @@ def block_scores(q, k) -> np.ndarray:
 
 
 def select_tiles(q, k, tq: TokenAttrs, tk: TokenAttrs, keep_percent: int, mode="R",
-                 heads=None) -> np.ndarray:
+                 heads=None, window=0) -> np.ndarray:
     """bool keep[h, u, t]: key tile t is attended by query pair u in head h.
 
     Non-video tiles are always True; of each pair's candidate video tiles the
@@ -93,7 +93,7 @@ def select_tiles(q, k, tq: TokenAttrs, tk: TokenAttrs, keep_percent: int, mode="
     nkt = -(-nk // BK)
     heads = list(range(q.shape[1])) if heads is None else list(heads)
     vid = video_tiles(tk)
-    cls = tile_classes(tq, tk, 128, BK, mode)
+    cls = tile_classes(tq, tk, 128, BK, mode, window=window)
     scores = block_scores(q, k)
     keep = np.ones((q.shape[1], n_pairs, nkt), bool)
     for u in range(n_pairs):

@@ -121,3 +121,70 @@ def test_sparse_rejected_by_backward():
     with pytest.raises(nm.NomasError) as e:
         nm.nomas_attn_bwd(plan, t, t, t, t, t, lse, t, t, t, SCALE, workspace=None)
     assert e.value.status == 3
+
+
+def test_sparse_with_window_480p_cached_step():
+    """Both options at once: a 2-segment window, then 25% of the remaining
+    video tiles; lists bit-exact and the attention against the oracle."""
+    need_gpu()
+    w = wl.cached_step_480p()
+    kc, vc = w.cache_kv()
+    cache = new_cache(16, w.n_cached + w.n_new)
+    fill_cache(cache, w.cached, dev(kc), dev(vc))
+    rows = stored_rows(w.cached)
+    keys = as_stored(w.cached) + w.new
+    q, kn, vn = w.q(3), w.k_new(3), w.v_new(3)
+    k, v = np.concatenate([kc[rows], kn]), np.concatenate([vc[rows], vn])
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16, window=2, video_keep_percent=25)
+    info = plan.info()
+    o, lse, ws = run(plan, cache, dev(q), dev(kn), dev(vn))
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    kept = sparse.select_tiles(q, k, tq, tk, 25, window=2)
+    cls = oracle.tile_classes(tq, tk, 128, 64, window=2)
+    lists = ws[:16 * info.sparse_list_entries * 4].view(torch.int32).cpu().numpy()
+    lists = lists.reshape(16, info.sparse_list_entries)
+    off = 0
+    for u in range(kept.shape[1]):
+        seen = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
+        n = int((kept[0, u] & seen).sum())
+        for h in range(16):
+            np.testing.assert_array_equal(lists[h, off:off + n] >> 4, np.flatnonzero(kept[h, u] & seen))
+        off += n
+    heads = [2, 9]
+    o_ref, l_ref = oracle.forward(q, k, v, tq, tk, SCALE, heads=heads, window=2, tile_keep=kept)
+    check_o(host(o)[:, heads], o_ref, "window 2 + sparse 25%")
+    check_lse(host(lse)[heads], l_ref, "window 2 + sparse 25%")
+
+
+@pytest.mark.timeout(600)
+def test_sparse_lists_bit_exact_720p_long_session():
+    """Long lists (about 1,900 key tiles per query pair): the bitonic sort at
+    2,048 entries, all heads, against the oracle's selection."""
+    need_gpu()
+    w = wl.long_session_720p()
+    kc, _ = w.cache_kv()
+    cache = new_cache(16, w.n_cached + w.n_new)
+    vz = np.zeros_like(kc)
+    fill_cache(cache, w.cached, dev(kc), dev(vz))
+    rows = stored_rows(w.cached)
+    keys = as_stored(w.cached) + w.new
+    q, kn = w.q(2), w.k_new(2)
+    k = np.concatenate([kc[rows], kn])
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16, video_keep_percent=25)
+    info = plan.info()
+    say(f"720p session, 25% of video tiles: {info.sparse_list_entries} entries per head")
+    _, _, ws = run(plan, cache, dev(q), dev(kn), dev(np.zeros_like(kn)))
+    lists = ws[:16 * info.sparse_list_entries * 4].view(torch.int32).cpu().numpy()
+    lists = lists.reshape(16, info.sparse_list_entries)
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    kept = sparse.select_tiles(q, k, tq, tk, 25)
+    cls = oracle.tile_classes(tq, tk, 128, 64)
+    off = 0
+    for u in range(kept.shape[1]):
+        seen = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
+        n = int((kept[0, u] & seen).sum())
+        for h in range(16):
+            np.testing.assert_array_equal(lists[h, off:off + n] >> 4, np.flatnonzero(kept[h, u] & seen),
+                                          err_msg=f"head {h} pair {u}")
+        off += n
+    assert off == info.sparse_list_entries
