@@ -103,6 +103,21 @@ def test_pack_backward_sliding_window(window):
     full_case(w.q_layout, 2, 8600 + window, window=window)
 
 
+def test_thirty_two_actions_backward():
+    """A segment with the largest action count (32) after a short history, as
+    a dense pack: all three gradients against the oracle."""
+    need_gpu()
+    g = np.random.default_rng(33)
+    acts = []
+    for a in range(32):
+        lo = int(g.integers(0, 4))
+        acts.append((int(g.integers(1, 4)), lo, int(g.integers(lo + 1, 5))))
+    segs = [wl.Segment(0, j, 1, 16, 2, [(1, 0, 1)]) for j in range(6)]
+    segs.append(wl.Segment(0, 6, 4, 16, 6, acts, n_pad=5))
+    say("32 actions, backward")
+    full_case(segs, 2, 8700)
+
+
 def test_ragged_pack_backward():
     """Token counts that are not multiples of the tile sizes, padding tokens,
     an odd number of 64-key tiles (last key-tile pair half missing)."""

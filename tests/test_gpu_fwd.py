@@ -175,6 +175,33 @@ def test_padding_rows_and_ragged_shapes():
     assert (host(o)[pad] == 0).all()
 
 
+def test_thirty_two_actions_and_many_cached_segments():
+    """The largest action count a segment may carry (32: every bit of the
+    descriptors' tail masks in use) and a cache of 40 small segments, as a
+    cached step, against the oracle."""
+    need_gpu()
+    g = np.random.default_rng(32)
+    acts = []
+    for a in range(32):
+        lo = int(g.integers(0, 4))
+        acts.append((int(g.integers(1, 4)), lo, int(g.integers(lo + 1, 5))))
+    big = wl.Segment(0, 40, 4, 16, 6, acts, n_pad=5)
+    cached = [wl.Segment(0, j, 1, 16, 2, [(1, 0, 1)]) for j in range(40)]
+    say(f"32 actions in one segment ({big.n_tokens} tokens) over 40 cached segments")
+    cache = new_cache(2, 40 * 19 + big.n_tokens)
+    kc = wl.randn((40 * 19, 2, 128), 3201)
+    vc = wl.randn((40 * 19, 2, 128), 3202)
+    fill_cache(cache, cached, dev(kc), dev(vc))
+    q, kn, vn = (wl.randn((big.n_tokens, 2, 128), 3203 + i) for i in range(3))
+    plan = nm.nomas_attn_plan([big], [big], cache, heads=2)
+    o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 2)
+    keys = cached + [big]
+    tq, tk = oracle.expand([big]), oracle.expand(keys)
+    o_ref, l_ref = oracle.forward(q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), tq, tk, SCALE)
+    check_o(host(o), o_ref, "32 actions, 40 cached segments")
+    check_lse(host(l), l_ref, "32 actions, 40 cached segments")
+
+
 def test_single_token_and_empty_query():
     need_gpu()
     s1 = [wl.Segment(0, 0, 1, 1, 0, [])]
