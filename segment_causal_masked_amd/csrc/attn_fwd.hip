@@ -20,7 +20,9 @@
 // computed in pieces whose un-normalised (O, max, sum) go to a workspace and
 // are merged by attn_fwd_combine_kernel.  Workgroup ids are remapped so that
 // the workgroups of one XCD take consecutive ranges, i.e. the q-tiles of the
-// same heads, which then share that XCD's L2 for their K/V.
+// same heads, which then share that XCD's L2 for their K/V.  A video-block
+// sparse plan gives every head its own key-tile lists (chosen on the device
+// before this kernel); the schedule is the same, only the list base moves.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, fp32 accumulate), per wave of
 // 32 queries:
