@@ -40,6 +40,10 @@ choice, never hidden):
   * sliding window (optional, mask.py rule 8): whole segments.
   * video-block sparsity (optional, sparse.py): which blocks are kept is
     stated there (pooled-sum block score in fp32, ties to the lower tile).
+  * camera cross-attention (camera.py, [Summary] Camera-Trajectory
+    Conditioning, Eq. 3): one camera token per latent frame, a video query
+    sees its own segment's camera tokens within a frame radius (all of them
+    by default); text rows get 0.
 
 Parity status: every function here is pinned by CPU tests (hand-built masks,
 closed forms, library special cases, finite differences, brute force) except
@@ -50,4 +54,4 @@ from .tokens import TokenAttrs, expand, V, H, A, PAD  # noqa: F401
 from .mask import visible_mask, visible_pair, brute_force_mask  # noqa: F401
 from .attention import forward, backward  # noqa: F401
 from .tiles import unmasked_pairs, tile_classes, EMPTY, FULL, PARTIAL  # noqa: F401
-from . import sparse  # noqa: F401
+from . import sparse, camera  # noqa: F401
