@@ -287,6 +287,74 @@ nomas_status nomas_kvcache_len(const nomas_kvcache* cache, int64_t* n_tokens,
 nomas_status nomas_kvcache_destroy(nomas_kvcache* cache);
 
 /* --------------------------------------------------------------------------
+ * Camera cross-attention ("Summary (Overview)", Model Architecture:
+ * Camera-Trajectory Conditioning, Eq. 3; gpts24.com, "Inside the
+ * Architecture: Dual Stream, Language Encoder, and Explicit Camera Math")
+ *
+ * Video tokens are the queries, camera tokens the keys and values; the
+ * result is what Eq. 3 adds to the video tokens.  A camera token stands for
+ * a group of four frames, i.e. one latent frame, so a segment of n_frames
+ * latent frames has n_frames camera tokens; the camera tokens of a layout
+ * are its segments' tokens concatenated in segment order (segment i's
+ * frame g is camera token c_i + g, c_i = sum of n_frames before i).
+ * Visibility (the pages state none; the reading taken): a video token of
+ * latent frame f in segment i sees camera tokens c_i + g of its own segment
+ * with |f - g| <= radius_frames; radius_frames < 0 means every camera token
+ * of segment i, and 0 the time-aligned reading (its own frame only).  Text
+ * and padding tokens are not queries: their output rows are written as 0.
+ * The projections (64-dim camera vectors to heads x 128, and of the output)
+ * are the caller's.
+ * ------------------------------------------------------------------------ */
+
+typedef struct nomas_camera_plan nomas_camera_plan;
+
+typedef struct {
+  int64_t n_queries;          /* tokens of the layout (rows of q and o)    */
+  int64_t n_video_queries;
+  int64_t n_camera_tokens;    /* sum of n_frames                           */
+  int64_t visible_pairs;      /* visible (video token, camera token) pairs */
+  double effective_flop;      /* 4 * 128 * heads * visible_pairs           */
+  double algorithmic_bytes;   /* q and o rows + k_cam and v_cam rows, bf16 */
+  int32_t num_heads;
+  int32_t radius_frames;      /* -1 = whole segment                        */
+} nomas_camera_plan_info;
+
+/* Build the per-token camera ranges of a query layout (records validated as
+ * for nomas_attn_plan) and, unless flags holds NOMAS_PLAN_HOST_ONLY, copy
+ * them to the current HIP device (synchronously).  *out is owned by the
+ * caller until nomas_camera_plan_destroy.
+ * Errors: INVALID_ARGUMENT (NULL pointer, num_heads < 1, unknown flag),
+ * LAYOUT, UNSUPPORTED (2^31 tokens or more), HIP. */
+nomas_status nomas_camera_attn_plan(const nomas_layout* q, int32_t num_heads,
+                                    int32_t radius_frames, int32_t flags,
+                                    nomas_camera_plan** out);
+
+nomas_status nomas_camera_plan_get_info(const nomas_camera_plan* plan,
+                                        nomas_camera_plan_info* info);
+
+/* Per query token, the camera tokens it sees: host_buf int32
+ * [n_queries][2] = {first, end} (first == end: none).  n must be >=
+ * 2 * n_queries. */
+nomas_status nomas_camera_plan_export_ranges(const nomas_camera_plan* plan,
+                                             int32_t* host_buf, size_t n);
+
+nomas_status nomas_camera_plan_destroy(nomas_camera_plan* plan);
+
+/* O = softmax(scale * Q K_cam^T + M) V_cam for every token of the plan's
+ * layout (0 for rows that see no camera token).
+ *   q, o          [n_queries][H][128] bf16, token strides q_stride / o_stride.
+ *   k_cam, v_cam  [n_camera_tokens][H][128] bf16, token stride cam_stride
+ *                 (may be NULL when the layout has no camera token).
+ * Enqueued on hip_stream; allocates nothing.
+ * Errors: INVALID_ARGUMENT (host-only plan, plan of another device, missing
+ * pointer, bad stride or scale), ALIGNMENT, HIP. */
+nomas_status nomas_camera_attn_fwd(const nomas_camera_plan* plan,
+                                   const void* q, int64_t q_stride,
+                                   const void* k_cam, const void* v_cam,
+                                   int64_t cam_stride, void* o, int64_t o_stride,
+                                   float scale, void* hip_stream);
+
+/* --------------------------------------------------------------------------
  * Errors
  * ------------------------------------------------------------------------ */
 

@@ -6,7 +6,9 @@ seeded workload descriptions.  Importing the package does not load the
 library; the first call does, and fails loudly if it is not built.
 """
 from ._lib import (  # noqa: F401
-    KVCache, NomasError, Plan, load,
+    CameraPlan, KVCache, NomasError, Plan, load,
+    nomas_camera_attn_fwd, nomas_camera_attn_plan, nomas_camera_plan_destroy,
+    nomas_camera_plan_export_ranges, nomas_camera_plan_get_info,
     nomas_attn_bwd, nomas_attn_bwd_workspace_size, nomas_attn_fwd,
     nomas_attn_fwd_workspace_size, nomas_attn_plan, nomas_kvcache_append,
     nomas_kvcache_create, nomas_kvcache_destroy, nomas_kvcache_len, nomas_kvcache_reset,

@@ -57,6 +57,13 @@ class nomas_plan_info(C.Structure):
                 ("video_keep_percent", C.c_int32), ("window_segments", C.c_int32)]
 
 
+class nomas_camera_plan_info(C.Structure):
+    _fields_ = [("n_queries", C.c_int64), ("n_video_queries", C.c_int64),
+                ("n_camera_tokens", C.c_int64), ("visible_pairs", C.c_int64),
+                ("effective_flop", C.c_double), ("algorithmic_bytes", C.c_double),
+                ("num_heads", C.c_int32), ("radius_frames", C.c_int32)]
+
+
 class NomasError(RuntimeError):
     def __init__(self, status, where, detail):
         self.status = status
@@ -91,6 +98,11 @@ def load():
         "nomas_kvcache_reset": [P],
         "nomas_kvcache_len": [P, C.POINTER(I64), C.POINTER(I32)],
         "nomas_kvcache_destroy": [P],
+        "nomas_camera_attn_plan": [C.POINTER(nomas_layout), I32, I32, I32, C.POINTER(P)],
+        "nomas_camera_plan_get_info": [P, C.POINTER(nomas_camera_plan_info)],
+        "nomas_camera_plan_export_ranges": [P, P, SZ],
+        "nomas_camera_plan_destroy": [P],
+        "nomas_camera_attn_fwd": [P, P, I64, P, P, I64, P, I64, F32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -182,6 +194,20 @@ class Plan:
     def __del__(self):
         if getattr(self, "handle", None) and self.handle.value and _lib is not None:
             _lib.nomas_plan_destroy(self.handle)
+            self.handle = C.c_void_p(0)
+
+
+class CameraPlan:
+    def __init__(self, handle, heads):
+        self.handle = C.c_void_p(handle)
+        self.heads = heads
+
+    def info(self) -> nomas_camera_plan_info:
+        return nomas_camera_plan_get_info(self)
+
+    def __del__(self):
+        if getattr(self, "handle", None) and self.handle.value and _lib is not None:
+            _lib.nomas_camera_plan_destroy(self.handle)
             self.handle = C.c_void_p(0)
 
 
@@ -308,6 +334,48 @@ def nomas_kvcache_len(cache):
     n, s = C.c_int64(), C.c_int32()
     _check(load().nomas_kvcache_len(cache.handle, C.byref(n), C.byref(s)), "nomas_kvcache_len")
     return n.value, s.value
+
+
+def nomas_camera_attn_plan(q_layout, *, heads=16, radius=-1, host_only=False) -> CameraPlan:
+    ql = _Layout(q_layout)
+    out = C.c_void_p()
+    _check(load().nomas_camera_attn_plan(C.byref(ql.c), heads, radius,
+                                         PLAN_HOST_ONLY if host_only else 0, C.byref(out)),
+           "nomas_camera_attn_plan")
+    return CameraPlan(out.value, heads)
+
+
+def nomas_camera_plan_get_info(plan) -> nomas_camera_plan_info:
+    info = nomas_camera_plan_info()
+    _check(load().nomas_camera_plan_get_info(plan.handle, C.byref(info)), "nomas_camera_plan_get_info")
+    return info
+
+
+def nomas_camera_plan_export_ranges(plan):
+    import numpy as np
+    info = nomas_camera_plan_get_info(plan)
+    buf = np.zeros((info.n_queries, 2), np.int32)
+    _check(load().nomas_camera_plan_export_ranges(plan.handle, buf.ctypes.data_as(C.c_void_p),
+                                                  buf.size), "nomas_camera_plan_export_ranges")
+    return buf
+
+
+def nomas_camera_plan_destroy(plan):
+    if plan.handle.value:
+        _check(load().nomas_camera_plan_destroy(plan.handle), "nomas_camera_plan_destroy")
+        plan.handle = C.c_void_p(0)
+
+
+def nomas_camera_attn_fwd(plan, q, k_cam, v_cam, o, scale=HEAD_DIM ** -0.5, stream=None):
+    h = plan.heads
+    qs = _token_stride(q, "q", h)
+    os_ = _token_stride(o, "o", h)
+    cs = _token_stride(k_cam, "k_cam", h)
+    if v_cam is not None and _token_stride(v_cam, "v_cam", h) != cs:
+        raise ValueError("k_cam and v_cam must share a token stride")
+    _check(load().nomas_camera_attn_fwd(plan.handle, _ptr(q), qs, _ptr(k_cam), _ptr(v_cam), cs,
+                                        _ptr(o), os_, float(scale), _stream_ptr(stream, q)),
+           "nomas_camera_attn_fwd")
 
 
 def nomas_status_string(status) -> str:

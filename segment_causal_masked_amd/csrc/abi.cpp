@@ -13,6 +13,7 @@
 #include "kernels.h"
 #include "nomas_attn.h"
 #include "plan.h"
+#include "status.h"
 
 namespace {
 
@@ -36,6 +37,11 @@ uint64_t next_cache_id() {
 }
 
 }  // namespace
+
+namespace nomas {
+nomas_status set_error(nomas_status s, const std::string& what) { return fail(s, what); }
+nomas_status clear_error() { return ok(); }
+}  // namespace nomas
 
 struct nomas_kvcache {
   int32_t heads = 0, head_dim = 0;
@@ -300,6 +306,10 @@ nomas_status nomas_plan_destroy(nomas_plan* p) {
 // forward
 // ---------------------------------------------------------------------------
 
+}  // extern "C"
+
+namespace {
+
 // Forward workspace: [sparse plans: kept lists [H][sp_total] int32 | key sums
 // [H][nkt][128] fp32 | query sums [H][n_pairs][128] fp32] [partial slots],
 // each part 256-byte aligned.
@@ -324,6 +334,10 @@ FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
   w.total = at;
   return w;
 }
+
+}  // namespace
+
+extern "C" {
 
 nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");

@@ -20,8 +20,8 @@ Token order inside a segment (the pages leave it open):
 
 Random numbers come from numpy's PCG64 with seed = the workload's seed base
 (1000, 2000, 3000, 4000, 5000 for the five workloads below, in order) + tensor
-id (Q=1, K=2, V=3, dO=4, windows=5, cache=6; the n-th of several denoising
-calls adds 10*n).  Values are N(0,1) rounded to bf16 (round-to-nearest-even) except
+id (Q=1, K=2, V=3, dO=4, windows=5, cache=6, camera K=7, camera V=8; the
+n-th of several denoising calls adds 10*n).  Values are N(0,1) rounded to bf16 (round-to-nearest-even) except
 the tiny fp32 case.
 """
 from __future__ import annotations
@@ -37,6 +37,7 @@ TPF_480P = 15 * 26   # 480x848 / 32
 TPF_720P = 22 * 40   # 704x1280 / 32
 
 TID_Q, TID_K, TID_V, TID_DO, TID_WIN, TID_CACHE = 1, 2, 3, 4, 5, 6
+TID_CAM_K, TID_CAM_V = 7, 8
 
 
 @dataclasses.dataclass
@@ -169,6 +170,16 @@ class Workload:
 
     def d_o(self, nfe=0):
         return self.tensor(TID_DO, self.n_q, nfe)
+
+    @property
+    def n_camera(self):
+        """Camera tokens of the query layout: one per latent frame."""
+        return int(sum(s.n_frames for s in self.q_layout))
+
+    def camera_kv(self, nfe=0):
+        """Camera-token K and V (already projected per head), [n_camera, H, D]."""
+        return (self.tensor(TID_CAM_K, self.n_camera, nfe),
+                self.tensor(TID_CAM_V, self.n_camera, nfe))
 
     def cache_kv(self, layer: int = 0):
         """Cached K and V as [n_cached, H, D] each (token-major)."""

@@ -262,3 +262,68 @@ def test_plan_sparse_rejects_out_of_range():
     for bad in (-1, 101):
         with pytest.raises(nm.NomasError):
             nm.nomas_attn_plan(segs, segs, heads=1, host_only=True, video_keep_percent=bad)
+
+
+# ---------------------------------------------------------------------------
+# camera cross-attention plan
+# ---------------------------------------------------------------------------
+
+def _ranges_to_mask(r, n_cam):
+    cols = np.arange(n_cam)
+    return (cols[None, :] >= r[:, :1]) & (cols[None, :] < r[:, 1:])
+
+
+@pytest.mark.parametrize("radius", [-1, 0, 1, 2, 5])
+def test_camera_plan_matches_oracle_random_layouts(radius):
+    from oracle.camera import camera_mask
+    g = np.random.default_rng(77 + radius)
+    for _ in range(60):
+        segs = random_tiny_layout(g, n_videos=int(g.integers(1, 4)))
+        p = nm.nomas_camera_attn_plan(segs, heads=2, radius=radius, host_only=True)
+        info = p.info()
+        m = camera_mask(segs, radius)
+        assert info.n_queries == m.shape[0] and info.n_camera_tokens == m.shape[1]
+        assert info.visible_pairs == int(m.sum())
+        assert info.radius_frames == (radius if radius >= 0 else -1)
+        r = nm.nomas_camera_plan_export_ranges(p)
+        np.testing.assert_array_equal(_ranges_to_mask(r, m.shape[1]), m)
+        assert np.all((r[:, 0] == r[:, 1]) | m.any(axis=1))
+
+
+@pytest.mark.parametrize("name", ["single_segment_480p", "training_pack_131k"])
+def test_camera_plan_workloads(name):
+    from oracle.camera import camera_layout
+    w = wl.WORKLOADS[name]()
+    p = nm.nomas_camera_attn_plan(w.q_layout, heads=16, radius=-1, host_only=True)
+    info = p.info()
+    q_seg, q_frame, c_seg, c_frame = camera_layout(w.q_layout)
+    assert info.n_queries == len(q_seg) and info.n_camera_tokens == len(c_seg)
+    assert info.n_video_queries == int((q_seg >= 0).sum())
+    per_seg = np.bincount(c_seg, minlength=len(w.q_layout))
+    assert info.visible_pairs == int(per_seg[q_seg[q_seg >= 0]].sum())
+    assert info.effective_flop == 4 * 128 * 16 * info.visible_pairs
+    r = nm.nomas_camera_plan_export_ranges(p)
+    vid = q_seg >= 0
+    starts = np.concatenate([[0], np.cumsum(per_seg)[:-1]])
+    np.testing.assert_array_equal(r[vid, 0], starts[q_seg[vid]])
+    np.testing.assert_array_equal(r[vid, 1], starts[q_seg[vid]] + per_seg[q_seg[vid]])
+    assert not r[~vid].any()
+
+
+def test_camera_plan_rejects_bad_arguments():
+    segs = [wl.Segment(0, 0, 2, 4, 1, [])]
+    with pytest.raises(nm.NomasError) as e:
+        nm.nomas_camera_attn_plan(segs, heads=0, host_only=True)
+    assert e.value.status == _lib.ERR_INVALID_ARGUMENT
+    bad = [wl.Segment(0, 0, 2, 4, 1, [(3, 1, 5)])]  # window past the last frame
+    with pytest.raises(nm.NomasError) as e:
+        nm.nomas_camera_attn_plan(bad, heads=1, host_only=True)
+    assert e.value.status == _lib.ERR_LAYOUT
+    p = nm.nomas_camera_attn_plan(segs, heads=1, host_only=True)
+    lib = nm.load()
+    assert lib.nomas_camera_attn_fwd(p.handle, None, 128, None, None, 128, None, 128,
+                                     C.c_float(0.1), None) == _lib.ERR_INVALID_ARGUMENT
+    assert "host-only" in nm.nomas_last_error()
+    buf = np.zeros(3, np.int32)
+    assert lib.nomas_camera_plan_export_ranges(p.handle, buf.ctypes.data_as(C.c_void_p),
+                                               buf.size) == _lib.ERR_INVALID_ARGUMENT
