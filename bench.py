@@ -229,6 +229,47 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches
             "caches_rotated": n_caches, "window_segments": window}
 
 
+def bench_camera(nm, wl, torch, iters=20, warmup=3):
+    """Camera cross-attention (Eq. 3) with every camera token of a segment
+    visible (radius -1): a 480p segment (3,280 tokens, 8 camera tokens) and
+    the 131072-token training pack.  HBM-bound: the figure of merit is the
+    algorithmic bytes (Q and O rows, camera K and V) per call time.  `iters`
+    back-to-back calls between two HIP events on the launch stream; the 480p
+    case rotates 12 query / output buffer pairs (322 MB, more than the 256 MB
+    last-level cache) so that rows come from HBM.  Inputs are drawn on the
+    device (timing only)."""
+    out = {}
+    for key, w, n_buf in (("segment_480p", wl.single_segment_480p(), 12),
+                          ("training_pack", wl.training_pack_131k(), 1)):
+        H, D = w.heads, 128
+        plan = nm.nomas_camera_attn_plan(w.q_layout, heads=H, radius=-1)
+        info = plan.info()
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7000)
+        rnd = lambda n: torch.randn((n, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        qs = [rnd(w.n_q) for _ in range(n_buf)]
+        outs = [torch.empty_like(qs[0]) for _ in range(n_buf)]
+        kc, vc = rnd(w.n_camera), rnd(w.n_camera)
+        stream = torch.cuda.current_stream()
+        for i in range(warmup):
+            nm.nomas_camera_attn_fwd(plan, qs[i % n_buf], kc, vc, outs[i % n_buf], D ** -0.5)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            nm.nomas_camera_attn_fwd(plan, qs[i % n_buf], kc, vc, outs[i % n_buf], D ** -0.5)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        gbs = info.algorithmic_bytes / (ms * 1e-3) / 1e9
+        out[key] = {"workload": w.name, "tokens": w.n_q, "video_tokens": int(info.n_video_queries),
+                    "camera_tokens": int(info.n_camera_tokens), "heads": H, "radius_frames": -1,
+                    "ms_per_call": round(ms, 4), "algorithmic_mb": round(info.algorithmic_bytes / 1e6, 2),
+                    "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "effective_tflops": round(info.effective_flop / (ms * 1e-3) / 1e12, 3),
+                    "buffers_rotated": n_buf, "calls_timed": iters}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +285,8 @@ def main():
                     help="skip the extra 480p step whose last two denoising calls are sparse")
     ap.add_argument("--no-sp8-share", action="store_true",
                     help="skip the extra rows at one GPU's share of 16 heads sharded over 8")
+    ap.add_argument("--no-camera", action="store_true",
+                    help="skip the camera cross-attention rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size first (untimed), as a known "
                          "quantity for calibrating HBM byte counters")
@@ -447,6 +490,8 @@ def main():
         if not args.no_training:
             share["training_pack"] = bench_training(nm, wl, torch, heads=2)
         line["sp8_share"] = share
+    if not args.no_camera:
+        line["camera_xattn"] = bench_camera(nm, wl, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
