@@ -16,13 +16,13 @@
 
 struct nomas_camera_plan {
   int32_t heads = 0, radius = 0;
-  int64_t nq = 0, n_video = 0, n_cam = 0, pairs = 0, n_blocks = 0;
+  int64_t nq = 0, n_video = 0, n_cam = 0, pairs = 0, n_groups = 0;
   std::vector<int32_t> ranges;   // [nq][2]: first, end camera token
-  std::vector<int32_t> branges;  // [n_blocks][2]: union over 32 query tokens
-  int device = -1;
+  std::vector<int32_t> granges;  // [n_groups][2]: union over CAM_GROUP query tokens
+  int device = -1, cus = 256;
   void* dmem = nullptr;
   const int2* d_qrange = nullptr;
-  const int2* d_brange = nullptr;
+  const int2* d_grange = nullptr;
 };
 
 namespace {
@@ -63,11 +63,12 @@ nomas_status build_ranges(const nomas_layout* q, nomas_camera_plan* p) {
     cam += F;
   }
   p->n_cam = cam;
-  p->n_blocks = (p->nq + 31) / 32;
-  p->branges.assign(size_t(2 * p->n_blocks), 0);
-  for (int64_t b = 0; b < p->n_blocks; ++b) {
+  const int64_t G = nomas::CAM_GROUP;
+  p->n_groups = (p->nq + G - 1) / G;
+  p->granges.assign(size_t(2 * p->n_groups), 0);
+  for (int64_t b = 0; b < p->n_groups; ++b) {
     int32_t lo = INT32_MAX, hi = INT32_MIN;
-    for (int64_t t = 32 * b; t < std::min(p->nq, 32 * b + 32); ++t) {
+    for (int64_t t = G * b; t < std::min(p->nq, G * b + G); ++t) {
       const int32_t a = p->ranges[size_t(2 * t)], z = p->ranges[size_t(2 * t + 1)];
       if (z > a) {
         lo = std::min(lo, a);
@@ -75,8 +76,8 @@ nomas_status build_ranges(const nomas_layout* q, nomas_camera_plan* p) {
       }
     }
     if (hi > lo) {
-      p->branges[size_t(2 * b)] = lo;
-      p->branges[size_t(2 * b + 1)] = hi;
+      p->granges[size_t(2 * b)] = lo;
+      p->granges[size_t(2 * b + 1)] = hi;
     }
   }
   return NOMAS_OK;
@@ -111,17 +112,18 @@ nomas_status nomas_camera_attn_plan(const nomas_layout* q, int32_t num_heads, in
   }
   if (!(flags & NOMAS_PLAN_HOST_ONLY)) {
     hipError_t e = hipGetDevice(&p->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&p->cus, hipDeviceAttributeMultiprocessorCount, p->device);
     if (e != hipSuccess) {
       delete p;
-      return hip_fail(e, "hipGetDevice");
+      return hip_fail(e, "device query");
     }
-    // query ranges padded to whole 32-token blocks (empty), then the block ranges
-    const size_t qbytes = size_t(p->n_blocks) * 32 * sizeof(int2);
+    // query ranges padded to whole groups (empty), then the group ranges
+    const size_t qbytes = size_t(p->n_groups) * nomas::CAM_GROUP * sizeof(int2);
     const size_t boff = (qbytes + 255) & ~size_t(255);
-    const size_t total = boff + std::max<size_t>(16, size_t(p->n_blocks) * sizeof(int2));
+    const size_t total = boff + std::max<size_t>(16, size_t(p->n_groups) * sizeof(int2));
     std::vector<char> staging(total, 0);
     if (!p->ranges.empty()) std::memcpy(staging.data(), p->ranges.data(), p->ranges.size() * 4);
-    if (!p->branges.empty()) std::memcpy(staging.data() + boff, p->branges.data(), p->branges.size() * 4);
+    if (!p->granges.empty()) std::memcpy(staging.data() + boff, p->granges.data(), p->granges.size() * 4);
     e = hipMalloc(&p->dmem, total);
     if (e == hipSuccess) e = hipMemcpy(p->dmem, staging.data(), total, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
@@ -130,7 +132,7 @@ nomas_status nomas_camera_attn_plan(const nomas_layout* q, int32_t num_heads, in
       return hip_fail(e, "camera plan upload");
     }
     p->d_qrange = reinterpret_cast<const int2*>(p->dmem);
-    p->d_brange = reinterpret_cast<const int2*>(static_cast<char*>(p->dmem) + boff);
+    p->d_grange = reinterpret_cast<const int2*>(static_cast<char*>(p->dmem) + boff);
   }
   *out = p;
   return clear_error();
@@ -195,15 +197,15 @@ nomas_status nomas_camera_attn_fwd(const nomas_camera_plan* p, const void* q, in
   cp.vc = static_cast<const uint16_t*>(v_cam);
   cp.o = static_cast<uint16_t*>(o);
   cp.qrange = p->d_qrange;
-  cp.brange = p->d_brange;
+  cp.grange = p->d_grange;
   cp.q_stride = q_stride;
   cp.cam_stride = cam_stride;
   cp.o_stride = o_stride;
   cp.nq = (int32_t)p->nq;
   cp.heads = p->heads;
-  cp.n_blocks = (int32_t)p->n_blocks;
+  cp.n_groups = (int32_t)p->n_groups;
   cp.scale_log2 = scale * 1.4426950408889634f;
-  e = nomas::launch_camera_attn(cp, static_cast<hipStream_t>(hip_stream));
+  e = nomas::launch_camera_attn(cp, p->cus, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "camera_attn_kernel launch");
   return clear_error();
 }

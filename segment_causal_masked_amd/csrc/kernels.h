@@ -94,20 +94,22 @@ struct BwdParams {
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
 
 // Camera cross-attention (camera.hip): query token t sees the camera tokens
-// [qrange[t].x, qrange[t].y); a block of 32 consecutive query tokens loops over
-// the union brange[block] of its tokens' ranges.
+// [qrange[t].x, qrange[t].y); a workgroup computes groups of CAM_GROUP
+// consecutive query tokens of one head, each over the union grange[group] of
+// its tokens' ranges; `cus` (compute units) sizes the grid.
+constexpr int CAM_GROUP = 128;
 struct CamParams {
   const uint16_t* q;       // [nq][H][128] bf16, stride q_stride
   const uint16_t* kc;      // [n_cam][H][128] bf16, stride cam_stride
   const uint16_t* vc;
   uint16_t* o;             // [nq][H][128] bf16, stride o_stride
-  const int2* qrange;      // n_blocks * 32 entries (tail: empty ranges)
-  const int2* brange;      // n_blocks entries
+  const int2* qrange;      // n_groups * CAM_GROUP entries (tail: empty ranges)
+  const int2* grange;      // n_groups entries
   int64_t q_stride, cam_stride, o_stride;
-  int32_t nq, heads, n_blocks;
+  int32_t nq, heads, n_groups;
   float scale_log2;        // softmax scale * log2(e)
 };
 
-hipError_t launch_camera_attn(const CamParams& p, hipStream_t stream);
+hipError_t launch_camera_attn(const CamParams& p, int cus, hipStream_t stream);
 
 }  // namespace nomas
