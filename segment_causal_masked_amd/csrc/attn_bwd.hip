@@ -107,24 +107,31 @@ static_assert(KV_STAGE_BYTES >= 4 * 64 * 64 * 4, "a stage holds one dV or dK hal
 // tiles (4 + 4 loads); wave 0 also the statistics, wave 1 the descriptors.
 __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt, char* stg,
                                                int w, int lane) {
-  const int r_in = lane >> 2;
-  const int cl = (lane & 3) ^ ((lane >> 4) & 3);
-  int row = qt * QT_ROWS + 16 * w + r_in;
-  row = row < p.nq ? row : p.nq - 1;
-  const int64_t off = (int64_t)row * p.q_stride + (int64_t)h * D + 8 * cl;
-#pragma unroll
-  for (int cg = 0; cg < 4; ++cg) {
-    dma16(p.q + off + 32 * cg, stg + cg * GRP128 + w * 1024);
-    dma16(p.d_o + off + 32 * cg, stg + QTILE_BYTES + cg * GRP128 + w * 1024);
-  }
-  const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + (int64_t)qt * QT_ROWS;
-  if (w == 0) {
-    const float* src = lane < 32 ? p.lse2 + srow + 4 * lane : p.delta + srow + 4 * (lane - 32);
-    dma16(src, stg + STAT_OFF);
+  const int qt0 = __builtin_amdgcn_readfirstlane(qt * QT_ROWS);
+  // statistics and descriptors first: a value the compiler reloads from
+  // scratch here then waits only for loads that have already landed, not for
+  // the Q / dO rows of this stage
+  const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qt0;
+  if (w == 0) {  // lanes 0..31: lse2, lanes 32..63: delta (each 32 x 16 B)
+    if (lane < 32) dma16_s(p.lse2 + srow, 16u * lane, stg + STAT_OFF);
+    else dma16_s(p.delta + srow, 16u * (lane - 32), stg + STAT_OFF);
   } else if (w == 1) {
-    const QDescDev* src = p.qdesc + (int64_t)qt * QT_ROWS + lane;
-    dma16(src, stg + QD_OFF);
-    dma16(src + 64, stg + QD_OFF + 1024);
+    const QDescDev* src = p.qdesc + qt0;
+    dma16_s(src, 16u * lane, stg + QD_OFF);
+    dma16_s(src + 64, 16u * lane, stg + QD_OFF + 1024);
+  }
+  // uniform row base (the q-tile's first row, head h) in SGPRs plus a 32-bit
+  // per-lane byte offset: row 16 w + lane / 4 of the tile (clamped to nq - 1),
+  // chunk (lane % 4) ^ ((lane / 16) % 4) of each 4-chunk group
+  const int64_t base = (int64_t)qt0 * p.q_stride + (int64_t)h * D;
+  const int r = min(16 * w + (lane >> 2), p.nq - 1 - qt0);
+  const uint32_t voff = (uint32_t)(r * (int)p.q_stride + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2u;
+  const uint16_t* qb = p.q + base;
+  const uint16_t* ob = p.d_o + base;
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {  // chunk group cg: 32 elements further along the row
+    dma16_s(qb + 32 * cg, voff, stg + cg * GRP128 + w * 1024);
+    dma16_s(ob + 32 * cg, voff, stg + QTILE_BYTES + cg * GRP128 + w * 1024);
   }
 }
 
@@ -135,8 +142,6 @@ struct KvWave {
   f32x16 dk[4];   // dK^T (unscaled)
   int kseg;
   uint32_t kbits;
-  int rbase[2];   // row-read base (Q / dO rows) for even / odd 16-dim steps
-  int tbase[2];   // transpose-read base for rows +0 / +4
 };
 
 // Visibility of this wave's 64 queries of the staged q-tile (query blocks
@@ -156,17 +161,23 @@ __device__ __forceinline__ uint32_t kv_vis_bits(const char* stg, int kseg, uint3
 
 // This wave's half of a staged q-tile (query blocks 2 qh, 2 qh + 1) against
 // its 32 keys; vis = all ones on FULL tiles.
-__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, uint32_t vis,
+// bases: this lane's {row-read base for even / odd 16-dim steps (Q / dO rows),
+// transpose-read base for rows +0 / +4}, kept in LDS rather than registers
+// (the wave is at its register limit; a spilled base would be reloaded from
+// scratch memory, and that wait would also drain the next stage's loads).
+__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4* bases, uint32_t vis,
                                          float scale_log2, int hh, int qh) {
   const char* qtile = stg;
   const char* dotile = stg + QTILE_BYTES;
+  const int4 lb = *bases;
+  const int rbase[2] = {lb.x, lb.y}, tbase[2] = {lb.z, lb.w};
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int b = 2 * qh + bb;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const int off = st.rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
+      const int off = rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
       const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qtile + off);
       const bf16x8 ado = *reinterpret_cast<const bf16x8*>(dotile + off);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, st.kf[ks], s, 0, 0, 0);
@@ -194,10 +205,10 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, uint32_t v
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int off = GRP128 * db + 1024 * (2 * b + half);
-        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + st.tbase[0]));
-        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + st.tbase[1]));
-        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + st.tbase[0]));
-        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + st.tbase[1]));
+        const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + tbase[0]));
+        const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(dotile + off + tbase[1]));
+        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + tbase[0]));
+        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4p)(qtile + off + tbase[1]));
         const bf16x8 at = __builtin_bit_cast(bf16x8, __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
         st.dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, pb[half], st.dv[db], 0, 0, 0);
@@ -228,6 +239,7 @@ __device__ __forceinline__ void kv_store(uint16_t* dst, const f32x16* acc, float
 __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char stg0[KV_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stg1[KV_STAGE_BYTES];
+  __shared__ int4 lane_bases[KV_THREADS];  // per-lane LDS read bases (see kv_qtile)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -264,13 +276,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
       st.dk[db] = f32x16{};
     }
     const int rrow = kmap(jq), rsw = (rrow >> 2) & 3;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) st.rbase[e] = rrow * 64 + 16 * ((2 * e + hh) ^ rsw);
     const int tr_j = (lane & 15) >> 2, tr_c4 = lane & 3;
     const int x = 2 * ((lane >> 4) & 1) + (tr_c4 >> 1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      st.tbase[r] = (8 * hh + tr_j + 4 * r) * 64 + 16 * (x ^ (2 * hh + r)) + 8 * (tr_c4 & 1);
+    lane_bases[tid] = int4{rrow * 64 + 16 * (hh ^ rsw), rrow * 64 + 16 * ((2 + hh) ^ rsw),
+                           (8 * hh + tr_j) * 64 + 16 * (x ^ (2 * hh)) + 8 * (tr_c4 & 1),
+                           (8 * hh + tr_j + 4) * 64 + 16 * (x ^ (2 * hh + 1)) + 8 * (tr_c4 & 1)};
   }
 
   const const_i32p ent = (const_i32p)p.kpair_idx + ((const_i32p)p.kpair_ptr)[u];
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
     // one code path for FULL and PARTIAL tiles (FULL: all bits set)
     const uint32_t vis = ((e >> sub) & 1) ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
-    kv_qtile(st, stg, vis, scale_log2, hh, qh);
+    kv_qtile(st, stg, lane_bases + tid, vis, scale_log2, hh, qh);
   };
   if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
   for (int t = 0; t < n_ent; t += 2) {

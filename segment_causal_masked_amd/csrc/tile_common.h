@@ -63,6 +63,16 @@ __device__ __forceinline__ void dma16(const void* gsrc, const void* lds_dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
+// The same load with a uniform base address in SGPRs and a 32-bit per-lane
+// byte offset: one VGPR per lane instead of a 64-bit pointer, which matters
+// in kernels at the edge of their register budget.  (No immediate offset:
+// the instruction's offset field moves the LDS destination as well.)
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)((const __attribute__((address_space(3))) char*)lds_dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier ordering LDS accesses only (no wait on global memory).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
