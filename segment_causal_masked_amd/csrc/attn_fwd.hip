@@ -58,8 +58,9 @@ constexpr int STAGE_BYTES = 2 * TILE_BYTES;
 // A half-wave's sum of P over its 32 keys above this value sends the wave to
 // the exact path (new reference = the row max); below it every P <= 2^16.
 constexpr float RESCALE_SUM = 65536.0f;
-// per partial piece: for each thread, 64 O values + max + sum
-constexpr int SLOT_FLOATS = NTHREADS * 66;
+// per partial piece, for each thread: its 64 O values divided by the piece's
+// row sum, as 32 bf16 pairs, then the piece's reference max and row sum (fp32)
+constexpr int SLOT_WORDS = NTHREADS * 34;
 
 struct WaveState {
   bf16x8 qf[8];     // Q fragment: query jq, dims [16 s + 8 hh, +8)
@@ -349,23 +350,28 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     if (slot < 0) {
       const float l_tot = ws.l_run + __shfl_xor(ws.l_run, 32);
       store_row(p, ws.acc, 0, 4, ws.m_run, l_tot, h, qrow, hh, true);
-    } else {  // partial piece: un-normalised state, thread-native layout
-      float* dst = p.partial + (int64_t)slot * SLOT_FLOATS + tid;
+    } else {  // partial piece: O / l (bf16) and (m, l), thread-native layout
+      const float l_tot = ws.l_run + __shfl_xor(ws.l_run, 32);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(p.partial) + (int64_t)slot * SLOT_WORDS + tid;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int ri = 0; ri < 16; ++ri) dst[(16 * db + ri) * NTHREADS] = ws.acc[db][ri];
-      dst[64 * NTHREADS] = ws.m_run;
-      dst[65 * NTHREADS] = ws.l_run;
+        for (int j = 0; j < 8; ++j)
+          dst[(8 * db + j) * NTHREADS] = (uint32_t)f2bf(ws.acc[db][2 * j] * inv) |
+                                         ((uint32_t)f2bf(ws.acc[db][2 * j + 1] * inv) << 16);
+      reinterpret_cast<float*>(dst)[32 * NTHREADS] = ws.m_run;
+      reinterpret_cast<float*>(dst)[33 * NTHREADS] = l_tot;
     }
     wait_vm_all();  // stores retired before the next piece's load accounting
     lds_barrier();  // the stage buffers are reused by the next piece
   }
 }
 
-// Merge the pieces of split units: O = sum_k 2^(m_k - m) O_k / sum_k 2^(m_k - m) l_k.
-// Workgroup (item, db, r) handles dims 32 db .. 32 db + 31 of rows 128 r ..
-// 128 r + 127 of one split unit; thread T mirrors forward thread 256 r + T.
+// Merge the pieces of split units: with a_k = 2^(m_k - m), m = max_k m_k,
+// O = sum_k a_k l_k (O_k / l_k) / sum_k a_k l_k.  Workgroup (item, db, r)
+// handles dims 32 db .. 32 db + 31 of rows 128 r .. 128 r + 127 of one split
+// unit; thread T mirrors forward thread 256 r + T.
 __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   const const_i32p cmb = (const_i32p)p.combine + 4 * (blockIdx.x >> 3);
   const int db = (blockIdx.x >> 1) & 3, r = blockIdx.x & 1;
@@ -376,26 +382,31 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   const int lane = T & 63;
   const int qrow = pr * UNIT_ROWS + (T >> 6) * 32 + (lane & 31);
   const int hh = lane >> 5;
-  const float* base = p.partial + (int64_t)first * SLOT_FLOATS + T;
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(p.partial) + (int64_t)first * SLOT_WORDS + T;
   float m = -INFINITY;
-  for (int k = 0; k < n; ++k) m = fmaxf(m, base[(int64_t)k * SLOT_FLOATS + 64 * NTHREADS]);
+  for (int k = 0; k < n; ++k)
+    m = fmaxf(m, __uint_as_float(base[(int64_t)k * SLOT_WORDS + 32 * NTHREADS]));
   const float mu = m == -INFINITY ? 0.f : m;
   f32x16 acc[1] = {f32x16{}};
   float l = 0.f;
   for (int k = 0; k < n; ++k) {
-    const float* src = base + (int64_t)k * SLOT_FLOATS;
-    const float a = __builtin_amdgcn_exp2f(src[64 * NTHREADS] - mu);
-    l += a * src[65 * NTHREADS];
+    const uint32_t* src = base + (int64_t)k * SLOT_WORDS;
+    const float wk = __builtin_amdgcn_exp2f(__uint_as_float(src[32 * NTHREADS]) - mu) *
+                     __uint_as_float(src[33 * NTHREADS]);
+    l += wk;
 #pragma unroll
-    for (int ri = 0; ri < 16; ++ri) acc[0][ri] += a * src[(16 * db + ri) * NTHREADS];
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t v = src[(8 * db + j) * NTHREADS];
+      acc[0][2 * j] += wk * __uint_as_float(v << 16);
+      acc[0][2 * j + 1] += wk * __uint_as_float(v & 0xffff0000u);
+    }
   }
-  const float l_tot = l + __shfl_xor(l, 32);
-  store_row(p, acc, db, 1, m, l_tot, h, qrow, hh, db == 0);
+  store_row(p, acc, db, 1, m, l, h, qrow, hh, db == 0);
 }
 
 }  // namespace
 
-size_t attn_fwd_slot_bytes() { return (size_t)SLOT_FLOATS * sizeof(float); }
+size_t attn_fwd_slot_bytes() { return (size_t)SLOT_WORDS * sizeof(uint32_t); }
 int attn_fwd_groups_per_cu() { return 1; }
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
