@@ -44,6 +44,9 @@ choice, never hidden):
     Conditioning, Eq. 3): one camera token per latent frame, a video query
     sees its own segment's camera tokens within a frame radius (all of them
     by default); text rows get 0.
+  * INT8 KV cache (int8cache.py, [Summary] Inference): per (head, token) row,
+    int8 codes and one power-of-two scale (the smallest keeping the codes
+    within +-127, round half to even); dequantized values are exact in bf16.
 
 Parity status: every function here is pinned by CPU tests (hand-built masks,
 closed forms, library special cases, finite differences, brute force) except
@@ -54,4 +57,4 @@ from .tokens import TokenAttrs, expand, V, H, A, PAD  # noqa: F401
 from .mask import visible_mask, visible_pair, brute_force_mask  # noqa: F401
 from .attention import forward, backward  # noqa: F401
 from .tiles import unmasked_pairs, tile_classes, EMPTY, FULL, PARTIAL  # noqa: F401
-from . import sparse, camera  # noqa: F401
+from . import sparse, camera, int8cache  # noqa: F401
