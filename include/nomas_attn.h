@@ -150,6 +150,7 @@ typedef struct {
 
 typedef struct nomas_plan nomas_plan;
 typedef struct nomas_kvcache nomas_kvcache;
+typedef struct nomas_kvcache_int8 nomas_kvcache_int8;
 
 /* Tile classes as exported by nomas_plan_export_classes. */
 enum { NOMAS_TILE_EMPTY = 0, NOMAS_TILE_FULL = 1, NOMAS_TILE_PARTIAL = 2 };
@@ -185,8 +186,11 @@ typedef struct {
  *   kv_new  key/value tokens passed to each call (k_new / v_new).
  *   cache   NULL, or a KV cache whose committed segments precede kv_new in
  *           key order: keys = cache tokens (in append order) ++ kv_new.
- *           The plan remembers the cache's current contents; after an append
- *           or truncate that changes them, calls return NOMAS_ERR_STALE_PLAN.
+ *           The plan remembers the cache's current contents (its segment
+ *           records, in order) and is valid with any cache of the same head
+ *           count holding exactly those segments -- this one, or another
+ *           layer's cache with the same history; after an append or truncate
+ *           that changes them, calls return NOMAS_ERR_STALE_PLAN.
  * Expands the records into per-token descriptors, classifies every
  * block_q x block_k tile as EMPTY, FULL or PARTIAL, builds per-q-tile and
  * per-k-tile lists of non-empty tiles and counts A, then (unless
@@ -216,8 +220,9 @@ nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* plan, size_t* bytes
 /* O = softmax(scale * Q K^T + M) V for the plan's queries.
  *   q, o          [n_queries][H][128], token strides q_stride / o_stride.
  *   k_new, v_new  [n_new_keys][H][128], token stride kv_stride.
- *   cache         the plan's cache (NULL iff the plan has none); its K/V
- *                 buffers supply keys [0, n_cached_keys).
+ *   cache         a cache holding the plan's cached segments (NULL iff the
+ *                 plan has none); its K/V buffers supply keys
+ *                 [0, n_cached_keys).
  *   lse           NULL or fp32 [H][n_queries].
  *   workspace     device memory of nomas_attn_fwd_workspace_size bytes
  *                 (may be NULL when that size is 0).
@@ -285,6 +290,52 @@ nomas_status nomas_kvcache_reset(nomas_kvcache* cache);
 nomas_status nomas_kvcache_len(const nomas_kvcache* cache, int64_t* n_tokens,
                                int32_t* n_segments);
 nomas_status nomas_kvcache_destroy(nomas_kvcache* cache);
+
+/* --------------------------------------------------------------------------
+ * INT8 KV cache ("Summary (Overview)", Inference: INT8 KV-cache quantization
+ * among the single-GPU optimisations; the scheme is not given)
+ *
+ * Rows are kept as the bf16 cache keeps them (each segment's video and head
+ * tokens, head-major), but quantized: a (head, token) row of 128 values x is
+ * stored as 128 int8 codes q and one int8 exponent e, where e is the smallest
+ * integer with max |x| <= 127 * 2^e (0 for a zero row, at least -127) and
+ * q = x / 2^e rounded to the nearest integer, ties to even.  The stored value
+ * q * 2^e is exact in bf16, so attention over it is exact attention over the
+ * dequantized cache.  Inputs must be finite.  About half the bytes of a bf16
+ * cache (129 B per row instead of 256).
+ *
+ * The attention kernels read bf16 tiles: nomas_kvcache_int8_expand writes the
+ * dequantized rows into a bf16 working cache once per (layer, segment step),
+ * and the four denoising calls of the step run on it; the INT8 caches are the
+ * resident archive of every layer.
+ * ------------------------------------------------------------------------ */
+
+/* k_codes / v_codes: caller-owned device memory, int8 [heads][capacity][128];
+ * k_exp / v_exp: int8 [heads][capacity]; all 16-byte aligned.  The handle is
+ * library-owned.  Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim != 128),
+ * ALIGNMENT. */
+nomas_status nomas_kvcache_int8_create(int32_t heads, int32_t head_dim, int64_t capacity,
+                                       void* k_codes, void* v_codes, void* k_exp,
+                                       void* v_exp, nomas_kvcache_int8** out);
+
+/* As nomas_kvcache_append, quantizing the stored rows on hip_stream. */
+nomas_status nomas_kvcache_int8_append(nomas_kvcache_int8* cache, const nomas_segment* seg,
+                                       const void* k_new, const void* v_new,
+                                       int64_t kv_stride, void* hip_stream);
+
+/* Make dst (a bf16 cache of the same head count) hold the dequantized rows
+ * and the segment records of cache: rows [0, len) of every head are written
+ * on hip_stream, dst's previous contents are replaced.  A plan built for
+ * these segments is valid with dst afterwards (also across layers).
+ * Errors: INVALID_ARGUMENT (NULL, head counts differ), CAPACITY (dst too
+ * small; nothing written), HIP. */
+nomas_status nomas_kvcache_int8_expand(const nomas_kvcache_int8* cache, nomas_kvcache* dst,
+                                       void* hip_stream);
+
+nomas_status nomas_kvcache_int8_truncate(nomas_kvcache_int8* cache, int32_t n_segments);
+nomas_status nomas_kvcache_int8_len(const nomas_kvcache_int8* cache, int64_t* n_tokens,
+                                    int32_t* n_segments);
+nomas_status nomas_kvcache_int8_destroy(nomas_kvcache_int8* cache);
 
 /* --------------------------------------------------------------------------
  * Camera cross-attention ("Summary (Overview)", Model Architecture:

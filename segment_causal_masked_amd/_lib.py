@@ -98,6 +98,12 @@ def load():
         "nomas_kvcache_reset": [P],
         "nomas_kvcache_len": [P, C.POINTER(I64), C.POINTER(I32)],
         "nomas_kvcache_destroy": [P],
+        "nomas_kvcache_int8_create": [I32, I32, I64, P, P, P, P, C.POINTER(P)],
+        "nomas_kvcache_int8_append": [P, C.POINTER(nomas_segment), P, P, I64, P],
+        "nomas_kvcache_int8_expand": [P, P, P],
+        "nomas_kvcache_int8_truncate": [P, I32],
+        "nomas_kvcache_int8_len": [P, C.POINTER(I64), C.POINTER(I32)],
+        "nomas_kvcache_int8_destroy": [P],
         "nomas_camera_attn_plan": [C.POINTER(nomas_layout), I32, I32, I32, C.POINTER(P)],
         "nomas_camera_plan_get_info": [P, C.POINTER(nomas_camera_plan_info)],
         "nomas_camera_plan_export_ranges": [P, P, SZ],
@@ -194,6 +200,21 @@ class Plan:
     def __del__(self):
         if getattr(self, "handle", None) and self.handle.value and _lib is not None:
             _lib.nomas_plan_destroy(self.handle)
+            self.handle = C.c_void_p(0)
+
+
+class KVCacheInt8:
+    """INT8 cache handle plus the caller-owned storage: codes [H][capacity][128]
+    and exponents [H][capacity], int8."""
+
+    def __init__(self, handle, k_codes, v_codes, k_exp, v_exp, heads, capacity):
+        self.handle = C.c_void_p(handle)
+        self.k_codes, self.v_codes, self.k_exp, self.v_exp = k_codes, v_codes, k_exp, v_exp
+        self.heads, self.capacity = heads, capacity
+
+    def __del__(self):
+        if getattr(self, "handle", None) and self.handle.value and _lib is not None:
+            _lib.nomas_kvcache_int8_destroy(self.handle)
             self.handle = C.c_void_p(0)
 
 
@@ -334,6 +355,49 @@ def nomas_kvcache_len(cache):
     n, s = C.c_int64(), C.c_int32()
     _check(load().nomas_kvcache_len(cache.handle, C.byref(n), C.byref(s)), "nomas_kvcache_len")
     return n.value, s.value
+
+
+def nomas_kvcache_int8_create(heads, capacity, device="cuda") -> KVCacheInt8:
+    """Allocates the int8 storage (torch tensors) and creates the handle."""
+    import torch
+    kc = torch.zeros((heads, capacity, HEAD_DIM), dtype=torch.int8, device=device)
+    vc = torch.zeros_like(kc)
+    ke = torch.zeros((heads, capacity), dtype=torch.int8, device=device)
+    ve = torch.zeros_like(ke)
+    out = C.c_void_p()
+    _check(load().nomas_kvcache_int8_create(heads, HEAD_DIM, capacity, _ptr(kc), _ptr(vc), _ptr(ke),
+                                            _ptr(ve), C.byref(out)), "nomas_kvcache_int8_create")
+    return KVCacheInt8(out.value, kc, vc, ke, ve, heads, capacity)
+
+
+def nomas_kvcache_int8_append(cache, segment, k_new, v_new, stream=None):
+    ks = _token_stride(k_new, "k_new", cache.heads)
+    if _token_stride(v_new, "v_new", cache.heads) != ks:
+        raise ValueError("k_new and v_new must share a token stride")
+    seg = to_c_segment(segment)
+    _check(load().nomas_kvcache_int8_append(cache.handle, C.byref(seg), _ptr(k_new), _ptr(v_new), ks,
+                                            _stream_ptr(stream, k_new)), "nomas_kvcache_int8_append")
+
+
+def nomas_kvcache_int8_expand(cache, dst, stream=None):
+    _check(load().nomas_kvcache_int8_expand(cache.handle, dst.handle, _stream_ptr(stream, dst.k_buf)),
+           "nomas_kvcache_int8_expand")
+
+
+def nomas_kvcache_int8_truncate(cache, n_segments):
+    _check(load().nomas_kvcache_int8_truncate(cache.handle, n_segments), "nomas_kvcache_int8_truncate")
+
+
+def nomas_kvcache_int8_len(cache):
+    n, s = C.c_int64(), C.c_int32()
+    _check(load().nomas_kvcache_int8_len(cache.handle, C.byref(n), C.byref(s)), "nomas_kvcache_int8_len")
+    return n.value, s.value
+
+
+def nomas_kvcache_int8_destroy(cache):
+    if cache.handle.value:
+        _check(load().nomas_kvcache_int8_destroy(cache.handle), "nomas_kvcache_int8_destroy")
+        cache.handle = C.c_void_p(0)
 
 
 def nomas_camera_attn_plan(q_layout, *, heads=16, radius=-1, host_only=False) -> CameraPlan:

@@ -31,11 +31,6 @@ nomas_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-uint64_t next_cache_id() {
-  static uint64_t id = 0;
-  return __atomic_add_fetch(&id, 1, __ATOMIC_RELAXED);
-}
-
 }  // namespace
 
 namespace nomas {
@@ -48,18 +43,20 @@ struct nomas_kvcache {
   int64_t capacity = 0, len = 0;
   void* k = nullptr;
   void* v = nullptr;
-  std::vector<nomas_segment> segs;
-  std::vector<uint64_t> serials;   // unique per appended segment
-  uint64_t next_serial = 1;
-  uint64_t id = 0;
+  std::vector<nomas_segment> segs;  // committed segments, in append order
+};
+
+struct nomas_kvcache_int8 {
+  int32_t heads = 0;
+  int64_t capacity = 0, len = 0;
+  void *k_codes = nullptr, *v_codes = nullptr, *k_exp = nullptr, *v_exp = nullptr;
+  std::vector<nomas_segment> segs;  // committed segments, in append order
 };
 
 struct nomas_plan {
   nomas::HostPlan host;
   bool has_cache = false;
-  uint64_t cache_id = 0;
-  int32_t cache_nseg = 0;
-  uint64_t cache_last_serial = 0;
+  std::vector<nomas_segment> cache_segs;  // the cache contents the plan was built for
   bool on_device = false;
   int device = -1;
   void* dmem = nullptr;
@@ -93,12 +90,15 @@ nomas_status hip_fail(hipError_t e, const char* where) {
   return fail(NOMAS_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// A plan encodes the layout only: it is valid for any cache of its head count
+// that holds exactly the segments it was built for (same identities and
+// records, same order), whichever cache object that is.
 bool plan_matches_cache(const nomas_plan* p, const nomas_kvcache* c) {
   if (!p->has_cache) return c == nullptr;
-  if (!c || c->id != p->cache_id) return false;
-  if ((int32_t)c->segs.size() != p->cache_nseg) return false;
-  const uint64_t last = c->serials.empty() ? 0 : c->serials.back();
-  return last == p->cache_last_serial;
+  if (!c || c->heads != p->host.heads || c->segs.size() != p->cache_segs.size()) return false;
+  for (size_t i = 0; i < c->segs.size(); ++i)
+    if (!nomas::same_segment(c->segs[i], p->cache_segs[i])) return false;
+  return true;
 }
 
 nomas_status check_stride(int64_t stride, int32_t heads, const char* name) {
@@ -176,9 +176,7 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
   }
   if (cache) {
     p->has_cache = true;
-    p->cache_id = cache->id;
-    p->cache_nseg = (int32_t)cache->segs.size();
-    p->cache_last_serial = cache->serials.empty() ? 0 : cache->serials.back();
+    p->cache_segs = cache->segs;
   }
   int groups = 256 * nomas::attn_fwd_groups_per_cu();  // host-only plans: MI355X's 256 CUs
   if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
@@ -538,7 +536,6 @@ nomas_status nomas_kvcache_create(int32_t heads, int32_t head_dim, int64_t capac
   c->capacity = capacity;
   c->k = k_buf;
   c->v = v_buf;
-  c->id = next_cache_id();
   *out = c;
   return ok();
 }
@@ -569,7 +566,6 @@ nomas_status nomas_kvcache_append(nomas_kvcache* c, const nomas_segment* seg, co
   hipError_t he = nomas::launch_kvcache_append(ap, static_cast<hipStream_t>(hip_stream));
   if (he != hipSuccess) return hip_fail(he, "kvcache_append launch");
   c->segs.push_back(*seg);
-  c->serials.push_back(c->next_serial++);
   c->len += n;
   return ok();
 }
@@ -579,7 +575,6 @@ nomas_status nomas_kvcache_truncate(nomas_kvcache* c, int32_t n_segments) {
   if (n_segments < 0 || n_segments > (int32_t)c->segs.size())
     return fail(NOMAS_ERR_INVALID_ARGUMENT, "n_segments out of range");
   c->segs.resize((size_t)n_segments);
-  c->serials.resize((size_t)n_segments);
   int64_t len = 0;
   for (const auto& s : c->segs) len += nomas::segment_cached_tokens(s);
   c->len = len;
@@ -596,6 +591,115 @@ nomas_status nomas_kvcache_len(const nomas_kvcache* c, int64_t* n_tokens, int32_
 }
 
 nomas_status nomas_kvcache_destroy(nomas_kvcache* c) {
+  delete c;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// INT8 KV cache
+// ---------------------------------------------------------------------------
+
+nomas_status nomas_kvcache_int8_create(int32_t heads, int32_t head_dim, int64_t capacity,
+                                       void* k_codes, void* v_codes, void* k_exp, void* v_exp,
+                                       nomas_kvcache_int8** out) {
+  if (!out) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (heads < 1) return fail(NOMAS_ERR_INVALID_ARGUMENT, "heads must be >= 1");
+  if (head_dim != NOMAS_HEAD_DIM) return fail(NOMAS_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (capacity < 0 || capacity > (int64_t(1) << 30)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "capacity out of range");
+  nomas_status s;
+  const bool need = capacity > 0;
+  if ((s = check_dev_ptr(k_codes, need, "k_codes")) || (s = check_dev_ptr(v_codes, need, "v_codes")) ||
+      (s = check_dev_ptr(k_exp, need, "k_exp")) || (s = check_dev_ptr(v_exp, need, "v_exp")))
+    return s;
+  nomas_kvcache_int8* c = new (std::nothrow) nomas_kvcache_int8();
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out of host memory");
+  c->heads = heads;
+  c->capacity = capacity;
+  c->k_codes = k_codes;
+  c->v_codes = v_codes;
+  c->k_exp = k_exp;
+  c->v_exp = v_exp;
+  *out = c;
+  return ok();
+}
+
+nomas_status nomas_kvcache_int8_append(nomas_kvcache_int8* c, const nomas_segment* seg,
+                                       const void* k_new, const void* v_new, int64_t kv_stride,
+                                       void* hip_stream) {
+  if (!c || !seg) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  std::string e = nomas::check_segment(*seg);
+  if (!e.empty()) return fail(NOMAS_ERR_LAYOUT, e);
+  for (const auto& s : c->segs)
+    if (s.video == seg->video && s.index == seg->index)
+      return fail(NOMAS_ERR_LAYOUT, "segment already in the cache");
+  const int64_t n = nomas::segment_cached_tokens(*seg);  // video + head rows, the first ones
+  if (c->len + n > c->capacity) return fail(NOMAS_ERR_CAPACITY, "append would exceed the cache capacity");
+  nomas_status s;
+  if ((s = check_dev_ptr(k_new, true, "k_new")) || (s = check_dev_ptr(v_new, true, "v_new"))) return s;
+  if ((s = check_stride(kv_stride, c->heads, "kv"))) return s;
+  nomas::Int8AppendParams ap{};
+  ap.k_src = static_cast<const uint16_t*>(k_new);
+  ap.v_src = static_cast<const uint16_t*>(v_new);
+  ap.k_codes = static_cast<int8_t*>(c->k_codes);
+  ap.v_codes = static_cast<int8_t*>(c->v_codes);
+  ap.k_exp = static_cast<int8_t*>(c->k_exp);
+  ap.v_exp = static_cast<int8_t*>(c->v_exp);
+  ap.src_stride = kv_stride;
+  ap.cap = c->capacity;
+  ap.dst_offset = c->len;
+  ap.tokens = (int32_t)n;
+  ap.heads = c->heads;
+  hipError_t he = nomas::launch_kvcache_int8_append(ap, static_cast<hipStream_t>(hip_stream));
+  if (he != hipSuccess) return hip_fail(he, "kvcache_int8_append launch");
+  c->segs.push_back(*seg);
+  c->len += n;
+  return ok();
+}
+
+nomas_status nomas_kvcache_int8_expand(const nomas_kvcache_int8* c, nomas_kvcache* dst,
+                                       void* hip_stream) {
+  if (!c || !dst) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (dst->heads != c->heads) return fail(NOMAS_ERR_INVALID_ARGUMENT, "caches differ in head count");
+  if (c->len > dst->capacity) return fail(NOMAS_ERR_CAPACITY, "destination cache too small");
+  nomas::Int8ExpandParams xp{};
+  xp.k_codes = static_cast<const int8_t*>(c->k_codes);
+  xp.v_codes = static_cast<const int8_t*>(c->v_codes);
+  xp.k_exp = static_cast<const int8_t*>(c->k_exp);
+  xp.v_exp = static_cast<const int8_t*>(c->v_exp);
+  xp.k_dst = static_cast<uint16_t*>(dst->k);
+  xp.v_dst = static_cast<uint16_t*>(dst->v);
+  xp.src_cap = c->capacity;
+  xp.dst_cap = dst->capacity;
+  xp.rows = c->len;
+  xp.heads = c->heads;
+  hipError_t he = nomas::launch_kvcache_int8_expand(xp, static_cast<hipStream_t>(hip_stream));
+  if (he != hipSuccess) return hip_fail(he, "kvcache_int8_expand launch");
+  dst->segs = c->segs;
+  dst->len = c->len;
+  return ok();
+}
+
+nomas_status nomas_kvcache_int8_truncate(nomas_kvcache_int8* c, int32_t n_segments) {
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (n_segments < 0 || n_segments > (int32_t)c->segs.size())
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "n_segments out of range");
+  c->segs.resize((size_t)n_segments);
+  int64_t len = 0;
+  for (const auto& s : c->segs) len += nomas::segment_cached_tokens(s);
+  c->len = len;
+  return ok();
+}
+
+nomas_status nomas_kvcache_int8_len(const nomas_kvcache_int8* c, int64_t* n_tokens,
+                                    int32_t* n_segments) {
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (n_tokens) *n_tokens = c->len;
+  if (n_segments) *n_segments = (int32_t)c->segs.size();
+  return ok();
+}
+
+nomas_status nomas_kvcache_int8_destroy(nomas_kvcache_int8* c) {
   delete c;
   return ok();
 }

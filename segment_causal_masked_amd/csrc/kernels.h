@@ -76,6 +76,28 @@ struct AppendParams {
 
 hipError_t launch_kvcache_append(const AppendParams& p, hipStream_t stream);
 
+// INT8 cache (kvcache.hip): per (head, token) row, 128 int8 codes and one
+// int8 exponent e, value = code * 2^e.
+struct Int8AppendParams {
+  const uint16_t* k_src;   // [T][H][128] bf16, stride src_stride
+  const uint16_t* v_src;
+  int8_t* k_codes;         // [H][cap][128]
+  int8_t* v_codes;
+  int8_t* k_exp;           // [H][cap]
+  int8_t* v_exp;
+  int64_t src_stride, cap, dst_offset;
+  int32_t tokens, heads;
+};
+hipError_t launch_kvcache_int8_append(const Int8AppendParams& p, hipStream_t stream);
+
+struct Int8ExpandParams {
+  const int8_t *k_codes, *v_codes, *k_exp, *v_exp;  // [H][src_cap][128], [H][src_cap]
+  uint16_t *k_dst, *v_dst;                          // bf16 [H][dst_cap][128]
+  int64_t src_cap, dst_cap, rows;                   // rows [0, rows) of every head
+  int32_t heads;
+};
+hipError_t launch_kvcache_int8_expand(const Int8ExpandParams& p, hipStream_t stream);
+
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *d_o;  // [T][H][128] bf16 (q, o, d_o: q_stride; k, v: kv_stride)
   const float* lse;        // [H][nq], natural log (from the forward)

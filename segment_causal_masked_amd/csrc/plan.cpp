@@ -61,6 +61,10 @@ static bool same_record(const nomas_segment& a, const nomas_segment& b) {
   return true;
 }
 
+bool same_segment(const nomas_segment& a, const nomas_segment& b) {
+  return a.video == b.video && a.index == b.index && same_record(a, b);
+}
+
 namespace {
 
 using Ident = std::pair<int32_t, int32_t>;  // (video, index)

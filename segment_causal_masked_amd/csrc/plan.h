@@ -107,6 +107,8 @@ struct CacheState {
 // Validate one record; returns "" or a description of the problem.
 std::string check_segment(const nomas_segment& s);
 int64_t segment_tokens(const nomas_segment& s);
+// Same identity (video, index) and the same record (sizes, action tails).
+bool same_segment(const nomas_segment& a, const nomas_segment& b);
 // Tokens of a segment that a KV cache keeps: its video and head tokens (the
 // first ones).  Action tails are visible only inside their own segment and
 // padding to nobody, so no later query can see them.

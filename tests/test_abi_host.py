@@ -327,3 +327,20 @@ def test_camera_plan_rejects_bad_arguments():
     buf = np.zeros(3, np.int32)
     assert lib.nomas_camera_plan_export_ranges(p.handle, buf.ctypes.data_as(C.c_void_p),
                                                buf.size) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_int8_cache_create_rejects_bad_arguments():
+    lib = nm.load()
+    out = C.c_void_p()
+    fake = C.c_void_p(0x10000)     # aligned, never dereferenced by create
+    odd = C.c_void_p(0x10001)
+    assert lib.nomas_kvcache_int8_create(0, 128, 16, fake, fake, fake, fake, C.byref(out)) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.nomas_kvcache_int8_create(2, 64, 16, fake, fake, fake, fake, C.byref(out)) == _lib.ERR_UNSUPPORTED
+    assert lib.nomas_kvcache_int8_create(2, 128, 16, fake, odd, fake, fake, C.byref(out)) == _lib.ERR_ALIGNMENT
+    assert lib.nomas_kvcache_int8_create(2, 128, 16, fake, fake, None, fake, C.byref(out)) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.nomas_kvcache_int8_create(2, 128, 16, fake, fake, fake, fake, None) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.nomas_kvcache_int8_create(2, 128, 16, fake, fake, fake, fake, C.byref(out)) == _lib.OK
+    n, s = C.c_int64(-1), C.c_int32(-1)
+    assert lib.nomas_kvcache_int8_len(out, C.byref(n), C.byref(s)) == _lib.OK and (n.value, s.value) == (0, 0)
+    assert lib.nomas_kvcache_int8_truncate(out, 1) == _lib.ERR_INVALID_ARGUMENT
+    assert lib.nomas_kvcache_int8_destroy(out) == _lib.OK
