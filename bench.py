@@ -229,6 +229,67 @@ def bench_long_session(nm, wl, torch, sessions=3, warmup=1, heads=None, n_caches
             "caches_rotated": n_caches, "window_segments": window}
 
 
+def bench_int8_session(nm, wl, torch, sessions=3, warmup=1):
+    """720p long session over an INT8 cache: per session the INT8 cache (16
+    cached segments) is expanded into a bf16 working cache, the 4 denoising
+    calls run on it, and the new segment is appended to the INT8 cache
+    (rolled back after each session).  In a model each layer keeps its own
+    INT8 cache and the working cache is shared by the layers: one expansion
+    per (layer, segment step).  Inputs are drawn on the device (timing only)."""
+    w = wl.long_session_720p()
+    H, D = w.heads, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4100)
+    rnd = lambda n: torch.randn((n, H, D), generator=g, device="cuda").to(torch.bfloat16)
+    cap = w.n_cached + w.n_new
+    c8 = nm.nomas_kvcache_int8_create(H, cap)
+    for s in w.cached:
+        nm.nomas_kvcache_int8_append(c8, s, rnd(s.n_tokens), rnd(s.n_tokens))
+    kb = torch.empty((H, cap, D), dtype=torch.bfloat16, device="cuda")
+    work = nm.nomas_kvcache_create(H, cap, kb, torch.empty_like(kb))
+    nm.nomas_kvcache_int8_expand(c8, work)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, work, heads=H)
+    A = plan.info().unmasked_pairs
+    rows, n_seg = nm.nomas_kvcache_int8_len(c8)
+    qs = [rnd(w.n_q) for _ in range(4)]
+    ks = [rnd(w.n_new) for _ in range(4)]
+    vs = [rnd(w.n_new) for _ in range(4)]
+    o = torch.empty((w.n_q, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(nm.nomas_attn_fwd_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    exp_ms, call_ms, app_ms, sess_ms = [], [], [], []
+    for it in range(warmup + sessions):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        ev[0].record(stream)
+        nm.nomas_kvcache_int8_expand(c8, work)
+        ev[1].record(stream)
+        for n in range(4):
+            nm.nomas_attn_fwd(plan, work, qs[n], ks[n], vs[n], o, lse, D ** -0.5, workspace=ws)
+            ev[n + 2].record(stream)
+        nm.nomas_kvcache_int8_append(c8, w.new[0], ks[3], vs[3])
+        ev[6].record(stream)
+        torch.cuda.synchronize()
+        nm.nomas_kvcache_int8_truncate(c8, n_seg)
+        if it >= warmup:
+            exp_ms.append(ev[0].elapsed_time(ev[1]))
+            call_ms += [ev[n + 1].elapsed_time(ev[n + 2]) for n in range(4)]
+            app_ms.append(ev[5].elapsed_time(ev[6]))
+            sess_ms.append(ev[0].elapsed_time(ev[6]))
+    e, c, a = float(np.mean(exp_ms)), float(np.mean(call_ms)), float(np.mean(app_ms))
+    exp_bytes = 2 * rows * H * (129 + 256)      # K and V: codes + exponent read, bf16 row written
+    app_rows = w.new[0].n_frames * w.new[0].tokens_per_frame + w.new[0].n_head
+    app_bytes = 2 * app_rows * H * (256 + 129)  # bf16 row read, codes + exponent written
+    return {"workload": w.name, "heads": H, "cached_rows": rows, "unmasked_pairs": A,
+            "int8_cache_mb": round(2 * cap * H * 129 / 1e6, 1),
+            "bf16_cache_mb": round(2 * cap * H * 256 / 1e6, 1),
+            "expand_ms": round(e, 4), "expand_gbs": round(exp_bytes / (e * 1e-3) / 1e9, 1),
+            "fwd_ms_per_call": round(c, 3),
+            "fwd_tflops": round(4.0 * D * H * A / (c * 1e-3) / 1e12, 2),
+            "int8_append_ms": round(a, 4), "int8_append_gbs": round(app_bytes / (a * 1e-3) / 1e9, 1),
+            "session_ms": round(float(np.mean(sess_ms)), 3), "sessions": sessions}
+
+
 def bench_camera(nm, wl, torch, iters=20, warmup=3):
     """Camera cross-attention (Eq. 3) with every camera token of a segment
     visible (radius -1): a 480p segment (3,280 tokens, 8 camera tokens) and
@@ -285,6 +346,8 @@ def main():
                     help="skip the extra 480p step whose last two denoising calls are sparse")
     ap.add_argument("--no-sp8-share", action="store_true",
                     help="skip the extra rows at one GPU's share of 16 heads sharded over 8")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the INT8-cache long-session row")
     ap.add_argument("--no-camera", action="store_true",
                     help="skip the camera cross-attention rows")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -490,6 +553,8 @@ def main():
         if not args.no_training:
             share["training_pack"] = bench_training(nm, wl, torch, heads=2)
         line["sp8_share"] = share
+    if not args.no_int8 and not args.no_long_session:
+        line["long_session_int8_cache"] = bench_int8_session(nm, wl, torch)
     if not args.no_camera:
         line["camera_xattn"] = bench_camera(nm, wl, torch)
     if not args.no_cpu_baseline:
