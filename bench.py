@@ -111,7 +111,41 @@ def cpu_baseline(w, runs=3):
             "kind": "oracle",
             "sample": f"one forward call of {w.name} ({w.heads} heads, {w.n_q} queries x "
                       f"{w.n_keys} keys), fp64 numpy, median of {runs} runs: {dt:.2f} s",
-            "cpu": cpu_model(), "blas": blas}
+            "cpu": cpu_model(), "blas": blas, "other_workloads": cpu_other_workloads()}
+
+
+def cpu_other_workloads():
+    """The oracle on the other forward shapes, for context: the single 480p
+    segment in full (one run) and a 256-query sample of one 720p long-session
+    call (all 16 heads, every key), scaled to the whole call by its share of
+    the unmasked pairs."""
+    import oracle
+    from segment_causal_masked_amd import workloads as wl
+    out = {}
+    w = wl.single_segment_480p()
+    tq = tk = oracle.expand(w.q_layout)
+    t0 = time.perf_counter()
+    oracle.forward(w.q(), w.k_new(), w.v_new(), tq, tk, 128 ** -0.5)
+    dt = time.perf_counter() - t0
+    a = oracle.unmasked_pairs(tq, tk)
+    out["single_segment_480p"] = {"seconds": round(dt, 3), "tflops": round(4.0 * 128 * w.heads * a / dt / 1e12, 6),
+                                  "sample": "whole call, one run"}
+    w = wl.long_session_720p()
+    keys = w.cached + w.new
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    rows = np.arange(w.n_q - 256, w.n_q)  # the last 256 queries (video, head and tail tokens)
+    kc, vc = w.cache_kv()
+    k = np.concatenate([kc, w.k_new()])
+    v = np.concatenate([vc, w.v_new()])
+    t0 = time.perf_counter()
+    oracle.forward(w.q(), k, v, tq, tk, 128 ** -0.5, rows=rows)
+    dt = time.perf_counter() - t0
+    a_rows = oracle.unmasked_pairs(tq.take(rows), tk)
+    a_all = oracle.unmasked_pairs(tq, tk)
+    out["long_session_720p"] = {"seconds_sample": round(dt, 3), "seconds_per_call_scaled": round(dt * a_all / a_rows, 1),
+                                "tflops": round(4.0 * 128 * w.heads * a_rows / dt / 1e12, 6),
+                                "sample": "256 of 7,232 queries, all keys and heads, one run"}
+    return out
 
 
 def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
