@@ -370,8 +370,7 @@ __device__ __forceinline__ uint32_t dq_vis_bits(const QDescDev& qd, const KDescD
   return v;
 }
 
-template <bool MASKED>
-__device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile,
+__device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile, bool masked,
                                         uint32_t vis, float scale_log2, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -405,13 +404,16 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
+    float pv[16];
+#pragma unroll
+    for (int ri = 0; ri < 16; ++ri) pv[ri] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, -st.lse2));
+    if (masked) {  // uniform: PARTIAL (or ragged) tiles only
+#pragma unroll
+      for (int ri = 0; ri < 16; ++ri) pv[ri] = ((vis >> (16 * kb + ri)) & 1u) ? pv[ri] : 0.f;
+    }
     bf16x8 dsb[2];
 #pragma unroll
-    for (int ri = 0; ri < 16; ++ri) {
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, -st.lse2));
-      if (MASKED) pv = ((vis >> (16 * kb + ri)) & 1u) ? pv : 0.f;
-      dsb[ri >> 3][ri & 7] = (__bf16)(pv * (dp[ri] - st.delta));
-    }
+    for (int ri = 0; ri < 16; ++ri) dsb[ri >> 3][ri & 7] = (__bf16)(pv[ri] * (dp[ri] - st.delta));
 
     // dQ^T += K^T dS^T over the two 16-key steps of this half
     auto tr = [&](int i) {  // i = 4 half + db
@@ -505,9 +507,11 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
     if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
     // one code path for FULL and PARTIAL tiles (a second variant would push
-    // the wave past its 256 registers): FULL tiles select with all bits set
-    const uint32_t vis = ((here >> half) & 1) ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
-    dq_tile<true>(st, cbuf, cbuf + TILE_BYTES, vis, scale_log2, hh);
+    // the wave past its 256 registers); the per-element mask sits behind a
+    // uniform branch that FULL tiles skip
+    const bool masked = (here >> half) & 1;
+    const uint32_t vis = masked ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
+    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, scale_log2, hh);
   };
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
