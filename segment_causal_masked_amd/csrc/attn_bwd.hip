@@ -125,7 +125,12 @@ __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt
   // chunk (lane % 4) ^ ((lane / 16) % 4) of each 4-chunk group
   const int64_t base = (int64_t)qt0 * p.q_stride + (int64_t)h * D;
   const int r = min(16 * w + (lane >> 2), p.nq - 1 - qt0);
-  const uint32_t voff = (uint32_t)(r * (int)p.q_stride + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2u;
+  // (the lane's chunk is recomputed here from a lane id the compiler cannot
+  // hoist: kept across the loop it is one more value to spill, and its
+  // reload from scratch would wait for the loads just issued)
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const uint32_t voff = (uint32_t)(r * (int)p.q_stride + 8 * ((ln & 3) ^ ((ln >> 4) & 3))) * 2u;
   const uint16_t* qb = p.q + base;
   const uint16_t* ob = p.d_o + base;
 #pragma unroll
