@@ -63,8 +63,9 @@ constexpr float RESCALE_SUM = 65536.0f;
 constexpr int SLOT_WORDS = NTHREADS * 34;
 
 struct WaveState {
-  bf16x8 qf[8];     // Q fragment: query jq, dims [16 s + 8 hh, +8)
+  bf16x8 qf[8];     // Q fragment, pre-scaled: query jq, dims [16 s + 8 hh, +8) of Q * scale * log2(e)
   f32x16 acc[4];    // O^T, dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
+  f32x16 negref;    // -reference in every register: the score chains start from it
   float m_run;      // reference max, log2 domain (same in both half-waves)
   float l_run;      // this half-wave's share of the running sum
   QDescDev qd;
@@ -73,12 +74,14 @@ struct WaveState {
 };
 
 // One 64-key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
+// With Q pre-scaled by scale * log2(e) and the score chains started from
+// -reference, the accumulators hold x = s * scale * log2(e) - ref directly:
+// P = exp2(x) needs no multiply-add per score.
 __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, const char* vtile,
-                                          const KDescDev* kd, bool masked, float scale_log2,
-                                          int hh) {
+                                          const KDescDev* kd, bool masked, int hh) {
   // S^T for keys 32 kb + (0..31): two independent accumulation chains,
   // interleaved, with the K fragments read four MFMAs ahead.
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+  f32x16 s[2];
   auto kfrag = [&](int i) {  // i = 2 ks + kb: row 32 kb + kmap(jq), chunk 2 ks + hh
     const int kb = i & 1, ks = i >> 1;
     return *reinterpret_cast<const bf16x8*>(ktile + ws.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
@@ -91,7 +94,8 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], ws.qf[i >> 1], s[i & 1], 0, 0, 0);
+    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i & 3], ws.qf[i >> 1], i < 2 ? ws.negref : s[i & 1],
+                                                       0, 0, 0);
     if (i + 4 < 16) kf[i & 3] = kfrag(i + 4);
   }
   // keep that order: the scheduler would otherwise sink each read next to
@@ -126,11 +130,12 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
         s[kb][ri] = visible(ws.qd, d.seg, d.bits) ? s[kb][ri] : -INFINITY;
       }
   }
-  // P = exp2(s * scale_log2 - m) in fp32 against the row's reference m,
-  // summed in fp32 (four chains) and rounded to bf16 as the P.V operand.
+  // P = exp2(x + d) in fp32, x = s * scale * log2(e) - ref as the chains left
+  // it and d = 0 (the common path) or old minus new reference, summed in fp32
+  // (four chains) and rounded to bf16 as the P.V operand.
   bf16x8 pf[4];  // P^T operand for step (kb, half) = 2 kb + half
   float l_half;  // this half-wave's sum over its 32 keys
-  auto probs = [&](float m_use) {
+  auto probs = [&](bool shift, float d) {
     float lsum[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -139,8 +144,8 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
         bf16x8 v;
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) {
-          const float pe = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(s[kb][8 * half + e8], scale_log2, -m_use));
+          const float x = s[kb][8 * half + e8];
+          const float pe = __builtin_amdgcn_exp2f(shift ? x + d : x);
           lsum[e8 & 3] = (kb | half | (e8 >> 2)) ? lsum[e8 & 3] + pe : pe;
           v[e8] = (__bf16)pe;
         }
@@ -155,9 +160,10 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   // maxima, and each such row -- only those, so a row's result depends on its
   // own scores alone -- takes max(reference, row max), rescales O and its sum
   // and forms P again (rows keeping their reference recompute the same P).
-  probs(ws.m_run == -INFINITY ? 0.f : ws.m_run);
+  probs(false, 0.f);
   const bool need_half = ws.m_run == -INFINITY || !(l_half <= RESCALE_SUM);
   if (__builtin_amdgcn_ballot_w64(need_half)) {
+    const float ref_old = ws.m_run == -INFINITY ? 0.f : ws.m_run;
     float t[12];
 #pragma unroll
     for (int j = 0; j < 5; ++j) t[j] = fmaxf(fmaxf(s[0][3 * j], s[0][3 * j + 1]), s[0][3 * j + 2]);
@@ -167,7 +173,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
     t[11] = s[1][15];
     const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
     const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(fmaxf(t[9], t[10]), t[11]);
-    const float m_half = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3) * scale_log2;
+    const float m_half = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3) + ref_old;
     const float m_row = fmaxf(m_half, __shfl_xor(m_half, 32));
     const bool need_row = need_half || __shfl_xor((int)need_half, 32);
     const float m_new = need_row ? fmaxf(ws.m_run, m_row) : ws.m_run;
@@ -176,7 +182,10 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
     ws.l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < 4; ++db) ws.acc[db] *= alpha;
-    probs(m_new == -INFINITY ? 0.f : m_new);
+    const float ref_new = m_new == -INFINITY ? 0.f : m_new;
+    probs(true, ref_old - ref_new);  // 0 for rows that keep their reference
+#pragma unroll
+    for (int ri = 0; ri < 16; ++ri) ws.negref[ri] = -ref_new;
   }
   ws.l_run += l_half;
 
@@ -306,10 +315,17 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     for (int db = 0; db < 4; ++db) ws.acc[db] = f32x16{};
     ws.m_run = -INFINITY;
     ws.l_run = 0.f;
+    ws.negref = f32x16{};  // reference 0 until the row has one
     // Q and the query descriptors must have arrived before the tile loop:
     // otherwise the compiler's own waits for them, placed inside the loop,
     // would also drain the tile prefetches issued below.
     wait_vm_all();
+    // Q * scale * log2(e), rounded to bf16 (one more rounding of Q, relative
+    // 2^-9, for no multiply per score in the tile loop)
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ws.qf[s8][e] = (__bf16)((float)ws.qf[s8][e] * scale_log2);
 
     auto issue_tile = [&](int kt, char* buf, KDescDev* kd) {
       issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // which the barrier has just released; one barrier per two tiles.
     auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) {
       if (!((here >> (2 + half)) & 1))  // not EMPTY for this wave's q-tile
-        tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, (here >> half) & 1, scale_log2, hh);
+        tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, (here >> half) & 1, hh);
     };
     auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
                     char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {

@@ -9,9 +9,13 @@ import segment_causal_masked_amd as nm
 
 SCALE = 128 ** -0.5
 
-# Gate from the method's brief: max-abs 1e-2 and mean-abs 1e-3 on unit-scale
-# outputs (inputs ~ N(0,1)); LSE is fp32 end to end, so a tighter bound holds.
-O_MAX_ABS, O_MEAN_ABS, LSE_ABS = 1e-2, 1e-3, 2e-3
+# Parity gate of the attention output: max-abs 1e-2 and mean-abs 1e-3 on
+# unit-scale outputs (inputs ~ N(0,1)).  LSE: the forward multiplies Q by
+# scale * log2(e) and rounds it to bf16 before the products, which moves a
+# score by at most 2^-9 * scale * sum_d |q_d k_d| (about 82 for N(0,1)
+# inputs: <= 1.4e-2 in natural-log units, ~1e-3 typical); the LSE, a soft
+# maximum of the scores, moves by a weighted mean of those shifts.  Gate 5e-3.
+O_MAX_ABS, O_MEAN_ABS, LSE_ABS = 1e-2, 1e-3, 5e-3
 
 
 def need_gpu():
