@@ -353,10 +353,12 @@ constexpr int Q_THREADS = 64 * Q_WAVES;
 constexpr int Q_STAGE_BYTES = 2 * TILE_BYTES;  // K | V of one 64-key tile
 
 struct QWave {
-  bf16x8 qf[8];    // Q row of this lane's query, dims [16 s + 8 hh, +8)
+  bf16x8 qf[8];    // Q row of this lane's query times scale * log2(e) (bf16, as
+                   // the forward rounds it), dims [16 s + 8 hh, +8)
   bf16x8 dof[8];   // dO row, same layout
   f32x16 acc[4];   // dQ^T (unscaled), dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
   float lse2, delta;
+  f32x16 neglse2;  // -lse2 in every register: the score chains start from it
   QDescDev qd;
   int kbase[2];    // K / V row-read base for even / odd 16-dim steps
   int tbase[2];    // K transpose-read base for rows +0 / +4
@@ -375,8 +377,10 @@ __device__ __forceinline__ uint32_t dq_vis_bits(const QDescDev& qd, const KDescD
   return v;
 }
 
+// With Q pre-scaled and the score chain started from -lse2, the accumulator
+// holds s * scale * log2(e) - lse2: P = exp2 of it, as in the forward.
 __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile, bool masked,
-                                        uint32_t vis, float scale_log2, int hh) {
+                                        uint32_t vis, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     // S^T and dP^T for keys 32 kb + (0..31): two chains, interleaved, with the
@@ -393,7 +397,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], ks == 0 ? st.neglse2 : s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[ks & 1], st.dof[ks], dp, 0, 0, 0);
       if (ks + 2 < 8) {
         fk[ks & 1] = rd(ktile, ks + 2);
@@ -411,7 +415,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
     float pv[16];
 #pragma unroll
-    for (int ri = 0; ri < 16; ++ri) pv[ri] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, -st.lse2));
+    for (int ri = 0; ri < 16; ++ri) pv[ri] = __builtin_amdgcn_exp2f(s[ri]);
     if (masked) {  // uniform: PARTIAL (or ragged) tiles only
 #pragma unroll
       for (int ri = 0; ri < 16; ++ri) pv[ri] = ((vis >> (16 * kb + ri)) & 1u) ? pv[ri] : 0.f;
@@ -502,6 +506,13 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
   const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
   wait_vm_all();  // rows and statistics in registers before the tile loads start
+  // Q * scale * log2(e) rounded to bf16, as the forward formed its scores
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.qf[s8][e] = (__bf16)((float)st.qf[s8][e] * scale_log2);
+#pragma unroll
+  for (int ri = 0; ri < 16; ++ri) st.neglse2[ri] = -st.lse2;
 
   // (always_inline: otherwise the wave state would be passed through scratch)
   auto issue_tile = [&](int kt, char* buf, KDescDev* kd) __attribute__((always_inline)) {
@@ -516,7 +527,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     // uniform branch that FULL tiles skip
     const bool masked = (here >> half) & 1;
     const uint32_t vis = masked ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
-    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, scale_log2, hh);
+    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, hh);
   };
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
