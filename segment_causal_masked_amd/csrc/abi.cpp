@@ -491,7 +491,7 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.dk = static_cast<uint16_t*>(dk);
   bp.dv = static_cast<uint16_t*>(dv);
   bp.delta = static_cast<float*>(workspace);
-  bp.lse2 = bp.delta + (size_t)h.heads * (size_t)h.nqt * 128;
+  bp.nlse2 = bp.delta + (size_t)h.heads * (size_t)h.nqt * 128;
   bp.qdesc = p->d_qdesc;
   bp.kdesc = p->d_kdesc;
   bp.pair_ptr = p->d_pair_ptr;

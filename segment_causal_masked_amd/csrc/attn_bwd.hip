@@ -56,7 +56,7 @@ __device__ __forceinline__ int xcd_major_unit(int b, int G) {
 // ---------------------------------------------------------------------------
 
 // 16 lanes per (head, query row) over rows 0 .. nqt * 128 - 1; rows past nq
-// (and rows that see no key, lse = -inf) get delta = 0 and lse2 = 0: they are
+// (and rows that see no key, lse = -inf) get delta = 0 and nlse2 = 0: they are
 // masked wherever they occur, so only finiteness matters there.
 __global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
   const int64_t rows = (int64_t)p.nqt * 128;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
   if (sub == 0) {
     p.delta[item] = acc;
     const float l = i < p.nq ? p.lse[(int64_t)h * p.nq + i] : -INFINITY;
-    p.lse2[item] = l == -INFINITY ? 0.f : l * LOG2E;
+    p.nlse2[item] = l == -INFINITY ? 0.f : -l * LOG2E;
   }
 }
 
@@ -97,13 +97,13 @@ constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int QT_ROWS = 128;
 constexpr int QTILE_BYTES = QT_ROWS * D * 2;         // 32 KB: a 128-row Q or dO tile
 constexpr int GRP128 = QT_ROWS * 64;                 // chunk-group stride of such a tile
-constexpr int STAT_OFF = 2 * QTILE_BYTES;            // lse2[128] | delta[128]
+constexpr int STAT_OFF = 2 * QTILE_BYTES;            // -lse2[128] | delta[128]
 constexpr int QD_OFF = STAT_OFF + 2 * QT_ROWS * 4;   // qdesc[128]
 constexpr int KV_STAGE_BYTES = QD_OFF + QT_ROWS * 16;
 static_assert(KV_STAGE_BYTES >= 4 * 64 * 64 * 4, "a stage holds one dV or dK half for the final sum");
 
 // Stage q-tile qt of head h: Q and dO rows (rows past nq read row nq - 1:
-// masked), lse2 / delta, query descriptors.  Wave w fills row group w of both
+// masked), -lse2 / delta, query descriptors.  Wave w fills row group w of both
 // tiles (4 + 4 loads); wave 0 also the statistics, wave 1 the descriptors.
 __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt, char* stg,
                                                int w, int lane) {
@@ -112,8 +112,8 @@ __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt
   // scratch here then waits only for loads that have already landed, not for
   // the Q / dO rows of this stage
   const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qt0;
-  if (w == 0) {  // lanes 0..31: lse2, lanes 32..63: delta (each 32 x 16 B)
-    if (lane < 32) dma16_s(p.lse2 + srow, 16u * lane, stg + STAT_OFF);
+  if (w == 0) {  // lanes 0..31: -lse2, lanes 32..63: delta (each 32 x 16 B)
+    if (lane < 32) dma16_s(p.nlse2 + srow, 16u * lane, stg + STAT_OFF);
     else dma16_s(p.delta + srow, 16u * (lane - 32), stg + STAT_OFF);
   } else if (w == 1) {
     const QDescDev* src = p.qdesc + qt0;
@@ -171,7 +171,7 @@ __device__ __forceinline__ uint32_t kv_vis_bits(const char* stg, int kseg, uint3
 // (the wave is at its register limit; a spilled base would be reloaded from
 // scratch memory, and that wait would also drain the next stage's loads).
 __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4* bases, uint32_t vis,
-                                         float scale_log2, int hh, int qh) {
+                                         int hh, int qh) {
   const char* qtile = stg;
   const char* dotile = stg + QTILE_BYTES;
   const int4 lb = *bases;
@@ -179,7 +179,19 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int b = 2 * qh + bb;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  With K
+    // pre-scaled, the score chain starts from -lse2 of those queries and
+    // ends at s * scale * log2(e) - lse2: P = exp2 of it.
+    f32x16 s, dp = f32x16{};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+      const float4 nl = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
+      s[4 * g] = nl.x;
+      s[4 * g + 1] = nl.y;
+      s[4 * g + 2] = nl.z;
+      s[4 * g + 3] = nl.w;
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int off = rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
@@ -188,18 +200,16 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, st.kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, st.vf[ks], dp, 0, 0, 0);
     }
-    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
-      const float4 lv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
       const float4 dv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
-      const float l2[4] = {lv.x, lv.y, lv.z, lv.w}, dl[4] = {dv.x, dv.y, dv.z, dv.w};
+      const float dl[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -l2[r]));
+        float pv = __builtin_amdgcn_exp2f(s[i]);
         pv = ((vis >> (16 * bb + i)) & 1u) ? pv : 0.f;
         pb[i >> 3][i & 7] = (__bf16)pv;
         dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl[r]));
@@ -291,13 +301,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   const const_i32p ent = (const_i32p)p.kpair_idx + ((const_i32p)p.kpair_ptr)[u];
   const int n_ent = ((const_i32p)p.kpair_ptr)[u + 1] - ((const_i32p)p.kpair_ptr)[u];
   wait_vm_all();  // K / V rows in registers before the stage loads start
+  // K * scale * log2(e) rounded to bf16: the score chains need no multiply
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.kf[s8][e] = (__bf16)((float)st.kf[s8][e] * scale_log2);
 
   auto compute = [&](int t, const char* stg) __attribute__((always_inline)) {
     const int e = ent[t];
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
     // one code path for FULL and PARTIAL tiles (FULL: all bits set)
     const uint32_t vis = ((e >> sub) & 1) ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
-    kv_qtile(st, stg, lane_bases + tid, vis, scale_log2, hh, qh);
+    kv_qtile(st, stg, lane_bases + tid, vis, hh, qh);
   };
   if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
   for (int t = 0; t < n_ent; t += 2) {
@@ -357,7 +372,7 @@ struct QWave {
                    // the forward rounds it), dims [16 s + 8 hh, +8)
   bf16x8 dof[8];   // dO row, same layout
   f32x16 acc[4];   // dQ^T (unscaled), dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
-  float lse2, delta;
+  float delta;
   f32x16 neglse2;  // -lse2 in every register: the score chains start from it
   QDescDev qd;
   int kbase[2];    // K / V row-read base for even / odd 16-dim steps
@@ -465,6 +480,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const float scale_log2 = p.scale_log2;
 
   QWave st;
+  float nl2;  // -lse2 of this lane's query
   {
     const int qr = qrow < p.nq ? qrow : p.nq - 1;  // rows past nq: computed, never stored
     const int64_t off = (int64_t)qr * p.q_stride + (int64_t)h * D + 8 * hh;
@@ -475,7 +491,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     }
     const bool in_tiles = qrow < p.nqt * QT_ROWS;
     const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qrow;
-    st.lse2 = in_tiles ? p.lse2[srow] : 0.f;
+    nl2 = in_tiles ? p.nlse2[srow] : 0.f;
     st.delta = in_tiles ? p.delta[srow] : 0.f;
     st.qd = in_tiles ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
 #pragma unroll
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.qf[s8][e] = (__bf16)((float)st.qf[s8][e] * scale_log2);
 #pragma unroll
-  for (int ri = 0; ri < 16; ++ri) st.neglse2[ri] = -st.lse2;
+  for (int ri = 0; ri < 16; ++ri) st.neglse2[ri] = nl2;
 
   // (always_inline: otherwise the wave state would be passed through scratch)
   auto issue_tile = [&](int kt, char* buf, KDescDev* kd) __attribute__((always_inline)) {

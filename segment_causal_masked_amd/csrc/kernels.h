@@ -103,7 +103,7 @@ struct BwdParams {
   const float* lse;        // [H][nq], natural log (from the forward)
   uint16_t *dq, *dk, *dv;  // outputs, same layouts as q / k / v
   float* delta;            // workspace [H][nqt*128]: rowsum(dO * O)
-  float* lse2;             // workspace [H][nqt*128]: lse * log2(e), 0 where -inf or padding
+  float* nlse2;            // workspace [H][nqt*128]: -lse * log2(e), 0 where -inf or padding
   const QDescDev* qdesc;   // nqt*128 entries
   const KDescDev* kdesc;   // nkt*64 entries
   const int32_t *pair_ptr, *pair_idx;    // per q-tile pair: the forward's key-tile lists
