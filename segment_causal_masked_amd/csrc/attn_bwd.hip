@@ -170,8 +170,8 @@ __device__ __forceinline__ uint32_t kv_vis_bits(const char* stg, int kseg, uint3
 // transpose-read base for rows +0 / +4}, kept in LDS rather than registers
 // (the wave is at its register limit; a spilled base would be reloaded from
 // scratch memory, and that wait would also drain the next stage's loads).
-__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4* bases, uint32_t vis,
-                                         int hh, int qh) {
+__device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4* bases, bool masked,
+                                         uint32_t vis, int hh, int qh) {
   const char* qtile = stg;
   const char* dotile = stg + QTILE_BYTES;
   const int4 lb = *bases;
@@ -192,6 +192,12 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
       s[4 * g + 2] = nl.z;
       s[4 * g + 3] = nl.w;
     }
+    // hidden pairs start at -inf and end there: P = 0 (uniform branch, so
+    // FULL tiles skip the selects)
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? s[i] : -INFINITY;
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int off = rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
@@ -209,8 +215,7 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        float pv = __builtin_amdgcn_exp2f(s[i]);
-        pv = ((vis >> (16 * bb + i)) & 1u) ? pv : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(s[i]);
         pb[i >> 3][i & 7] = (__bf16)pv;
         dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl[r]));
       }
@@ -310,9 +315,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto compute = [&](int t, const char* stg) __attribute__((always_inline)) {
     const int e = ent[t];
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
-    // one code path for FULL and PARTIAL tiles (FULL: all bits set)
-    const uint32_t vis = ((e >> sub) & 1) ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
-    kv_qtile(st, stg, lane_bases + tid, vis, hh, qh);
+    const bool masked = (e >> sub) & 1;
+    const uint32_t vis = masked ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
+    kv_qtile(st, stg, lane_bases + tid, masked, vis, hh, qh);
   };
   if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
   for (int t = 0; t < n_ent; t += 2) {
