@@ -30,7 +30,8 @@
  *     failure nomas_last_error() holds a thread-local description;
  *   - Q, K, V, O, dO, dQ, dK, dV are bf16, token-major [tokens][heads][128]
  *     with the 128 dims contiguous and a caller-given token stride (elements,
- *     >= heads*128, multiple of 8); device pointers must be 16-byte aligned;
+ *     >= heads*128, multiple of 8, at most 2^24: larger ones return
+ *     INVALID_ARGUMENT); device pointers must be 16-byte aligned;
  *   - LSE is fp32 [heads][queries] (natural log; -inf for a row that sees no
  *     key);
  *   - device work is enqueued on the caller's HIP stream (NULL = default

@@ -105,6 +105,9 @@ nomas_status check_stride(int64_t stride, int32_t heads, const char* name) {
   if (stride < (int64_t)heads * NOMAS_HEAD_DIM)
     return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " stride < heads * 128");
   if (stride % 8 != 0) return fail(NOMAS_ERR_ALIGNMENT, std::string(name) + " stride not a multiple of 8");
+  // the kernels form a block's per-lane offsets (up to 63 rows) in 32 bits
+  if (stride > (int64_t(1) << 24))
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " stride above 2^24 elements");
   return NOMAS_OK;
 }
 

@@ -517,8 +517,8 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   lc.n_cached = 0;
   lc.lane_row = 16 * (w & 3) + (lane >> 2);
   lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  lc.lane_cache = lc.lane_row * D + 8 * lc.lane_chunk;
-  lc.lane_new = (int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk;
+  lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
+  lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
   lc.k_cache_h = p.k + (int64_t)h * D;  // unused: no cached keys
   lc.v_cache_h = p.v + (int64_t)h * D;
   lc.k_new_h = p.k + (int64_t)h * D;
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   auto issue_tile = [&](int kt, char* buf, KDescDev* kd) __attribute__((always_inline)) {
     issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
     issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
-    if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
+    if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
   };
   auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
     if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile

@@ -276,8 +276,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
   lc.n_cached = p.n_cached;
   lc.lane_row = 16 * (w & 3) + (lane >> 2);
   lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  lc.lane_cache = lc.lane_row * D + 8 * lc.lane_chunk;
-  lc.lane_new = (int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk;
+  lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
+  lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
 
   for (int pc = pc0; pc < pc1; ++pc) {
     const int unit = pieces[4 * pc];
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     auto issue_tile = [&](int kt, char* buf, KDescDev* kd) {
       issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
       issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
-      if (w == 0 && lane < 32) dma16(p.kdesc + kt * BK + 2 * lane, kd);
+      if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
     };
     if (n_ent > 0) issue_tile(ent_at(0) >> 4, sbuf0, skd0);
     if (n_ent > 1) issue_tile(ent_at(1) >> 4, sbuf1, skd1);

@@ -181,6 +181,8 @@ nomas_status nomas_camera_attn_fwd(const nomas_camera_plan* p, const void* q, in
     if (!st.needed) continue;
     if (st.v < row) return set_error(NOMAS_ERR_INVALID_ARGUMENT, std::string(st.name) + " stride < heads * 128");
     if (st.v % 8 != 0) return set_error(NOMAS_ERR_ALIGNMENT, std::string(st.name) + " stride not a multiple of 8");
+    if (st.v > (int64_t(1) << 24))
+      return set_error(NOMAS_ERR_INVALID_ARGUMENT, std::string(st.name) + " stride above 2^24 elements");
   }
   struct Ptr { const void* v; const char* name; bool needed; };
   for (const Ptr& pt : {Ptr{q, "q", true}, Ptr{o, "o", true}, Ptr{k_cam, "k_cam", p->n_cam > 0},

@@ -98,7 +98,8 @@ struct LoadCtx {
   int64_t kv_stride;                      // new-token stride (elements)
   int32_t nk, n_cached;
   int32_t lane_row, lane_chunk;           // this lane's row / chunk inside a block
-  int32_t lane_cache, lane_new;           // element offsets of (lane_row, lane_chunk)
+  uint32_t lane_cache, lane_new;          // byte offsets of (lane_row, lane_chunk) from a
+                                          // block's first row (cache / new-token rows)
 };
 
 __device__ __forceinline__ void issue_half(const LoadCtx& c, const uint16_t* cache_h,
@@ -106,20 +107,25 @@ __device__ __forceinline__ void issue_half(const LoadCtx& c, const uint16_t* cac
   const int k0 = kt * BK;
   const int gq = w >> 2;
   char* d = dst + 4096 * gq + 1024 * (w & 3);
-  const uint16_t* src;
+  // Whole blocks of cache or new-token rows: a uniform base (SGPRs) plus the
+  // lane's loop-invariant byte offset, so no per-lane address arithmetic.
   if (k0 + BK <= c.n_cached) {
-    src = cache_h + (int64_t)k0 * D + c.lane_cache;
+    const uint16_t* sb = cache_h + (int64_t)k0 * D + 32 * gq;
+    dma16_s(sb, c.lane_cache, d);
+    dma16_s(sb + 64, c.lane_cache, d + 8192);
   } else if (k0 >= c.n_cached && k0 + BK <= c.nk) {
-    src = new_h + (int64_t)(k0 - c.n_cached) * c.kv_stride + c.lane_new;
+    const uint16_t* sb = new_h + (int64_t)(k0 - c.n_cached) * c.kv_stride + 32 * gq;
+    dma16_s(sb, c.lane_new, d);
+    dma16_s(sb + 64, c.lane_new, d + 8192);
   } else {  // straddles the cache / new boundary or runs past the last key
     int key = k0 + c.lane_row;
     key = key < c.nk ? key : c.nk - 1;  // any valid row: masked later
-    src = (key < c.n_cached ? cache_h + (int64_t)key * D
-                            : new_h + (int64_t)(key - c.n_cached) * c.kv_stride) + 8 * c.lane_chunk;
+    const uint16_t* src = (key < c.n_cached ? cache_h + (int64_t)key * D
+                                            : new_h + (int64_t)(key - c.n_cached) * c.kv_stride) +
+                          8 * c.lane_chunk + 32 * gq;
+    dma16(src, d);
+    dma16(src + 64, d + 8192);
   }
-  src += 32 * gq;
-  dma16(src, d);
-  dma16(src + 64, d + 8192);
 }
 
 }  // namespace

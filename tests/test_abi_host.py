@@ -165,6 +165,10 @@ def test_host_only_plan_cannot_run_and_cache_checks():
     assert lib.nomas_kvcache_create(1, 128, 10, C.c_void_p(256), C.c_void_p(512), C.byref(c)) == 0
     assert lib.nomas_kvcache_create(1, 128, 10, C.c_void_p(258), C.c_void_p(512),
                                     C.byref(C.c_void_p())) == _lib.ERR_ALIGNMENT
+    # token strides above 2^24 elements are refused before any device work
+    fits = _lib.to_c_segment(seg(actions=[]))  # 10 cached rows: fits
+    st = lib.nomas_kvcache_append(c, C.byref(fits), C.c_void_p(256), C.c_void_p(256), (1 << 24) + 8, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "2^24" in nm.nomas_last_error()
     big = _lib.to_c_segment(seg(n_frames=3, tokens_per_frame=4, actions=[]))  # 14 tokens > 10
     st = lib.nomas_kvcache_append(c, C.byref(big), C.c_void_p(256), C.c_void_p(256), 128, None)
     assert st == _lib.ERR_CAPACITY
