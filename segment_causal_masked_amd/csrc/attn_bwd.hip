@@ -471,6 +471,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) KDescDev skd1[BK];
   __shared__ __attribute__((aligned(16))) KDescDev skd2[BK];
   __shared__ __attribute__((aligned(16))) KDescDev skd3[BK];
+  // LDS byte addresses of the stage buffers, for the staging loads
+  const uint32_t lb0 = lds_addr(sbuf0), lb1 = lds_addr(sbuf1), lb2 = lds_addr(sbuf2), lb3 = lds_addr(sbuf3);
+  const uint32_t lk0 = lds_addr(skd0), lk1 = lds_addr(skd1), lk2 = lds_addr(skd2), lk3 = lds_addr(skd3);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   for (int ri = 0; ri < 16; ++ri) st.neglse2[ri] = nl2;
 
   // (always_inline: otherwise the wave state would be passed through scratch)
-  auto issue_tile = [&](int kt, char* buf, KDescDev* kd) __attribute__((always_inline)) {
+  auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) __attribute__((always_inline)) {
     issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
     issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
     if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   };
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
-                  char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) __attribute__((always_inline)) {
+                  uint32_t n0, uint32_t nk0, uint32_t n1, uint32_t nk1) __attribute__((always_inline)) {
     const int last = n_ent - 1;
     const int e0 = ent[t], e1 = ent[min(t + 1, last)];
     int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
@@ -565,11 +568,11 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     tile(e0, b0, k0);
     if (t + 1 < n_ent) tile(e1, b1, k1);
   };
-  if (n_ent > 0) issue_tile(ent[0] >> 4, sbuf0, skd0);
-  if (n_ent > 1) issue_tile(ent[1] >> 4, sbuf1, skd1);
+  if (n_ent > 0) issue_tile(ent[0] >> 4, lb0, lk0);
+  if (n_ent > 1) issue_tile(ent[1] >> 4, lb1, lk1);
   for (int t = 0; t < n_ent; t += 4) {
-    pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
-    if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, sbuf0, skd0, sbuf1, skd1);
+    pair(t, sbuf0, skd0, sbuf1, skd1, lb2, lk2, lb3, lk3);
+    if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, lb0, lk0, lb1, lk1);
   }
 
   if (qrow < p.nq) {

@@ -239,6 +239,9 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
   __shared__ __attribute__((aligned(16))) KDescDev skd1[BK];
   __shared__ __attribute__((aligned(16))) KDescDev skd2[BK];
   __shared__ __attribute__((aligned(16))) KDescDev skd3[BK];
+  // LDS byte addresses of the stage buffers, for the staging loads
+  const uint32_t lb0 = lds_addr(sbuf0), lb1 = lds_addr(sbuf1), lb2 = lds_addr(sbuf2), lb3 = lds_addr(sbuf3);
+  const uint32_t lk0 = lds_addr(skd0), lk1 = lds_addr(skd1), lk2 = lds_addr(skd2), lk3 = lds_addr(skd3);
   static_assert(NSTAGE == 4, "the unrolled loop below names four stage buffers");
 
   const int tid = threadIdx.x;
@@ -327,13 +330,13 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) ws.qf[s8][e] = (__bf16)((float)ws.qf[s8][e] * scale_log2);
 
-    auto issue_tile = [&](int kt, char* buf, KDescDev* kd) {
+    auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) {
       issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
       issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
       if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
     };
-    if (n_ent > 0) issue_tile(ent_at(0) >> 4, sbuf0, skd0);
-    if (n_ent > 1) issue_tile(ent_at(1) >> 4, sbuf1, skd1);
+    if (n_ent > 0) issue_tile(ent_at(0) >> 4, lb0, lk0);
+    if (n_ent > 1) issue_tile(ent_at(1) >> 4, lb1, lk1);
 
     // Tiles go in pairs: iteration j computes tiles 2j, 2j+1 (buffers of one
     // half of the ring) after issuing tiles 2j+2, 2j+3 into the other half,
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
         tile_step(ws, cbuf, cbuf + TILE_BYTES, ckd, (here >> half) & 1, hh);
     };
     auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
-                    char* n0, KDescDev* nk0, char* n1, KDescDev* nk1) {
+                    uint32_t n0, uint32_t nk0, uint32_t n1, uint32_t nk1) {
       // the four entries this pair needs, read before the barrier (their
       // scalar-load latency then overlaps the wait instead of following it)
       const int last = n_ent - 1;
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
       if (t + 1 < n_ent) tile(e1, b1, k1);
     };
     for (int t = 0; t < n_ent; t += 4) {
-      pair(t, sbuf0, skd0, sbuf1, skd1, sbuf2, skd2, sbuf3, skd3);
-      if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, sbuf0, skd0, sbuf1, skd1);
+      pair(t, sbuf0, skd0, sbuf1, skd1, lb2, lk2, lb3, lk3);
+      if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, lb0, lk0, lb1, lk1);
     }
 
     if (slot < 0) {

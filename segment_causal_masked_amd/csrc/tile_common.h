@@ -73,6 +73,23 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const 
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
+// LDS byte address of a __shared__ object.  Taken once, from the object
+// itself, so that staging code carries 32-bit LDS addresses in SGPRs instead
+// of 64-bit generic pointers (and their null checks) for every stage buffer.
+__device__ __forceinline__ uint32_t lds_addr(const void* shared_obj) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)shared_obj);
+}
+
+// dma16 / dma16_s with the LDS destination given as an LDS byte address.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier ordering LDS accesses only (no wait on global memory).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -102,11 +119,12 @@ struct LoadCtx {
                                           // block's first row (cache / new-token rows)
 };
 
+// dst: LDS byte address of the half-tile (K or V) buffer.
 __device__ __forceinline__ void issue_half(const LoadCtx& c, const uint16_t* cache_h,
-                                           const uint16_t* new_h, char* dst, int kt, int w) {
+                                           const uint16_t* new_h, uint32_t dst, int kt, int w) {
   const int k0 = kt * BK;
   const int gq = w >> 2;
-  char* d = dst + 4096 * gq + 1024 * (w & 3);
+  const uint32_t d = dst + 4096u * gq + 1024u * (w & 3);
   // Whole blocks of cache or new-token rows: a uniform base (SGPRs) plus the
   // lane's loop-invariant byte offset, so no per-lane address arithmetic.
   if (k0 + BK <= c.n_cached) {
