@@ -198,6 +198,8 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? s[i] : -INFINITY;
     }
+    // the S / dP chains run at raised priority (as the forward's S^T block)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int off = rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
@@ -206,6 +208,7 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, st.kf[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, st.vf[ks], dp, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -415,6 +418,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
       fk[i] = rd(ktile, i);
       fv[i] = rd(vtile, i);
     }
+    __builtin_amdgcn_s_setprio(1);  // as the forward's S^T block
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], ks == 0 ? st.neglse2 : s, 0, 0, 0);
@@ -431,6 +435,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_s_setprio(0);
 
     // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
     float pv[16];

@@ -89,8 +89,9 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   bf16x8 kf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
-  // A wave issuing its MFMA block runs at raised priority, so that the other
+  // A wave issuing its S^T block runs at raised priority, so that the other
   // wave of the SIMD fills the gaps with its softmax instead of competing.
+  // (The P.V block runs at normal priority: raising it there too is slower.)
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -189,7 +190,6 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const char* ktile, cons
   }
   ws.l_run += l_half;
 
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     ws.acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 3], pf[i >> 2], ws.acc[i & 3], 0, 0, 0);
