@@ -451,7 +451,7 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
 
 nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  // delta and lse * log2(e) per (head, query row of the padded q-tiles)
+  // delta and -lse * log2(e) per (head, query row of the padded q-tiles)
   *bytes = 2 * (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
   return ok();
 }

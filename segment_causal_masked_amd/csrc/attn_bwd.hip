@@ -8,7 +8,7 @@
 //   delta = rowsum(dO * O),  dS = P * (dP - delta),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // Three launches on one stream:
-//   1. bwd_rowstats_kernel: delta and lse * log2(e) per (head, query);
+//   1. bwd_rowstats_kernel: delta and -lse * log2(e) per (head, query);
 //   2. bwd_dkdv_kernel: one workgroup per pair of 64-key tiles of a head
 //      (eight waves, two per SIMD: four key groups of 32 keys x two halves of
 //      each q-tile), looping over the q-tiles that see those keys (the union
