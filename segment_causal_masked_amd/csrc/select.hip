@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void select_lists_kernel(SelParams p) {
   __shared__ float qs[128];
   __shared__ uint64_t keys[SELECT_MAX_ENTRIES];
   __shared__ uint8_t keep[SELECT_MAX_ENTRIES];
-  __shared__ int counts[256];
+  __shared__ int wave_tot[4];
   const int e0 = p.pair_ptr[u], n = p.pair_ptr[u + 1] - e0;
   if (tid < 128) qs[tid] = p.q_sum[((int64_t)h * p.n_pairs + u) * 128 + tid];
   int npow = 1;
@@ -160,18 +160,20 @@ __global__ __launch_bounds__(256) void select_lists_kernel(SelParams p) {
   const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
   int c = 0;
   for (int i = c0; i < c1; ++i) c += keep[i];
-  counts[tid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int v = counts[t];
-      counts[t] = run;
-      run += v;
-    }
+  // exclusive prefix sum of c over the 256 threads: inclusive scan inside
+  // each wave, then the totals of the waves before this one
+  const int lane = tid & 63;
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
   }
+  if (lane == 63) wave_tot[tid >> 6] = incl;
   __syncthreads();
-  int32_t* out = p.lists + (int64_t)h * p.sp_total + p.sp_ptr[u] + counts[tid];
+  int before = incl - c;
+  for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
+  int32_t* out = p.lists + (int64_t)h * p.sp_total + p.sp_ptr[u] + before;
   for (int i = c0; i < c1; ++i)
     if (keep[i]) *out++ = p.pair_idx[e0 + i];
 }
