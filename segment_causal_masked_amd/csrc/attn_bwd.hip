@@ -171,7 +171,7 @@ __device__ __forceinline__ uint32_t kv_vis_bits(const char* stg, int kseg, uint3
 // (the wave is at its register limit; a spilled base would be reloaded from
 // scratch memory, and that wait would also drain the next stage's loads).
 __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4* bases, bool masked,
-                                         uint32_t vis, int hh, int qh) {
+                                         uint32_t vis, float scale_log2, int hh, int qh) {
   const char* qtile = stg;
   const char* dotile = stg + QTILE_BYTES;
   const int4 lb = *bases;
@@ -179,24 +179,14 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int b = 2 * qh + bb;
-    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  With K
-    // pre-scaled, the score chain starts from -lse2 of those queries and
-    // ends at s * scale * log2(e) - lse2: P = exp2 of it.
-    f32x16 s, dp = f32x16{};
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
-      const float4 nl = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
-      s[4 * g] = nl.x;
-      s[4 * g + 1] = nl.y;
-      s[4 * g + 2] = nl.z;
-      s[4 * g + 3] = nl.w;
-    }
-    // hidden pairs start at -inf and end there: P = 0 (uniform branch, so
-    // FULL tiles skip the selects)
+    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  Hidden pairs
+    // start their score chain at -inf and end there: P = 0 (uniform branch,
+    // so FULL tiles skip the selects).  K is not pre-scaled here: the
+    // scores keep the rounding of the forward's, whose lse they meet.
+    f32x16 s = f32x16{}, dp = f32x16{};
     if (masked) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? s[i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? 0.f : -INFINITY;
     }
     // the S / dP chains run at raised priority (as the forward's S^T block)
     __builtin_amdgcn_s_setprio(1);
@@ -213,12 +203,13 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+      const float4 nl = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
       const float4 dv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
-      const float dl[4] = {dv.x, dv.y, dv.z, dv.w};
+      const float nl2[4] = {nl.x, nl.y, nl.z, nl.w}, dl[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        const float pv = __builtin_amdgcn_exp2f(s[i]);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, nl2[r]));
         pb[i >> 3][i & 7] = (__bf16)pv;
         dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl[r]));
       }
@@ -309,18 +300,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   const const_i32p ent = (const_i32p)p.kpair_idx + ((const_i32p)p.kpair_ptr)[u];
   const int n_ent = ((const_i32p)p.kpair_ptr)[u + 1] - ((const_i32p)p.kpair_ptr)[u];
   wait_vm_all();  // K / V rows in registers before the stage loads start
-  // K * scale * log2(e) rounded to bf16: the score chains need no multiply
-#pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.kf[s8][e] = (__bf16)((float)st.kf[s8][e] * scale_log2);
 
   auto compute = [&](int t, const char* stg) __attribute__((always_inline)) {
     const int e = ent[t];
     if ((e >> (2 + sub)) & 1) return;  // no visible pair for this key tile
     const bool masked = (e >> sub) & 1;
     const uint32_t vis = masked ? kv_vis_bits(stg, st.kseg, st.kbits, hh, qh) : ~0u;
-    kv_qtile(st, stg, lane_bases + tid, masked, vis, hh, qh);
+    kv_qtile(st, stg, lane_bases + tid, masked, vis, scale_log2, hh, qh);
   };
   if (n_ent > 0) kv_issue_stage(p, h, ent[0] >> 4, stg0, w, lane);
   for (int t = 0; t < n_ent; t += 2) {
