@@ -451,7 +451,7 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
 
 nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  // delta and -lse * log2(e) per (head, query row of the padded q-tiles)
+  // -delta and -lse * log2(e) per (head, query row of the padded q-tiles)
   *bytes = 2 * (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
   return ok();
 }
@@ -493,8 +493,8 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.dq = static_cast<uint16_t*>(dq);
   bp.dk = static_cast<uint16_t*>(dk);
   bp.dv = static_cast<uint16_t*>(dv);
-  bp.delta = static_cast<float*>(workspace);
-  bp.nlse2 = bp.delta + (size_t)h.heads * (size_t)h.nqt * 128;
+  bp.ndelta = static_cast<float*>(workspace);
+  bp.nlse2 = bp.ndelta + (size_t)h.heads * (size_t)h.nqt * 128;
   bp.qdesc = p->d_qdesc;
   bp.kdesc = p->d_kdesc;
   bp.pair_ptr = p->d_pair_ptr;

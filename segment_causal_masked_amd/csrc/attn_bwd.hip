@@ -8,7 +8,7 @@
 //   delta = rowsum(dO * O),  dS = P * (dP - delta),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 // Three launches on one stream:
-//   1. bwd_rowstats_kernel: delta and -lse * log2(e) per (head, query);
+//   1. bwd_rowstats_kernel: -delta and -lse * log2(e) per (head, query);
 //   2. bwd_dkdv_kernel: one workgroup per pair of 64-key tiles of a head
 //      (eight waves, two per SIMD: four key groups of 32 keys x two halves of
 //      each q-tile), looping over the q-tiles that see those keys (the union
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 1);
   if (sub == 0) {
-    p.delta[item] = acc;
+    p.ndelta[item] = -acc;
     const float l = i < p.nq ? p.lse[(int64_t)h * p.nq + i] : -INFINITY;
     p.nlse2[item] = l == -INFINITY ? 0.f : -l * LOG2E;
   }
@@ -97,7 +97,7 @@ constexpr int KV_THREADS = 64 * KV_WAVES;
 constexpr int QT_ROWS = 128;
 constexpr int QTILE_BYTES = QT_ROWS * D * 2;         // 32 KB: a 128-row Q or dO tile
 constexpr int GRP128 = QT_ROWS * 64;                 // chunk-group stride of such a tile
-constexpr int STAT_OFF = 2 * QTILE_BYTES;            // -lse2[128] | delta[128]
+constexpr int STAT_OFF = 2 * QTILE_BYTES;            // -lse2[128] | -delta[128]
 constexpr int QD_OFF = STAT_OFF + 2 * QT_ROWS * 4;   // qdesc[128]
 constexpr int KV_STAGE_BYTES = QD_OFF + QT_ROWS * 16;
 static_assert(KV_STAGE_BYTES >= 4 * 64 * 64 * 4, "a stage holds one dV or dK half for the final sum");
@@ -112,9 +112,9 @@ __device__ __forceinline__ void kv_issue_stage(const BwdParams& p, int h, int qt
   // scratch here then waits only for loads that have already landed, not for
   // the Q / dO rows of this stage
   const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qt0;
-  if (w == 0) {  // lanes 0..31: -lse2, lanes 32..63: delta (each 32 x 16 B)
+  if (w == 0) {  // lanes 0..31: -lse2, lanes 32..63: -delta (each 32 x 16 B)
     if (lane < 32) dma16_s(p.nlse2 + srow, 16u * lane, stg + STAT_OFF);
-    else dma16_s(p.delta + srow, 16u * (lane - 32), stg + STAT_OFF);
+    else dma16_s(p.ndelta + srow, 16u * (lane - 32), stg + STAT_OFF);
   } else if (w == 1) {
     const QDescDev* src = p.qdesc + qt0;
     dma16_s(src, 16u * lane, stg + QD_OFF);
@@ -183,7 +183,17 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
     // start their score chain at -inf and end there: P = 0 (uniform branch,
     // so FULL tiles skip the selects).  K is not pre-scaled here: the
     // scores keep the rounding of the forward's, whose lse they meet.
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // the dP chain starts from -delta of those queries and ends at dP - delta
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+      const float4 nd = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
+      dp[4 * g] = nd.x;
+      dp[4 * g + 1] = nd.y;
+      dp[4 * g + 2] = nd.z;
+      dp[4 * g + 3] = nd.w;
+    }
     if (masked) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? 0.f : -INFINITY;
@@ -204,14 +214,13 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
     for (int g = 0; g < 4; ++g) {
       const int q0 = 32 * b + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
       const float4 nl = *reinterpret_cast<const float4*>(stg + STAT_OFF + 4 * q0);
-      const float4 dv = *reinterpret_cast<const float4*>(stg + STAT_OFF + 512 + 4 * q0);
-      const float nl2[4] = {nl.x, nl.y, nl.z, nl.w}, dl[4] = {dv.x, dv.y, dv.z, dv.w};
+      const float nl2[4] = {nl.x, nl.y, nl.z, nl.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, nl2[r]));
         pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl[r]));
+        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
       }
     }
 #pragma unroll
@@ -366,8 +375,8 @@ struct QWave {
                    // the forward rounds it), dims [16 s + 8 hh, +8)
   bf16x8 dof[8];   // dO row, same layout
   f32x16 acc[4];   // dQ^T (unscaled), dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
-  float delta;
-  f32x16 neglse2;  // -lse2 in every register: the score chains start from it
+  f32x16 negdelta;  // -delta in every register: the dP chains start from it
+  f32x16 neglse2;   // -lse2 in every register: the score chains start from it
   QDescDev qd;
   int kbase[2];    // K / V row-read base for even / odd 16-dim steps
   int tbase[2];    // K transpose-read base for rows +0 / +4
@@ -394,7 +403,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
   for (int kb = 0; kb < 2; ++kb) {
     // S^T and dP^T for keys 32 kb + (0..31): two chains, interleaved, with the
     // K / V row fragments read two MFMA pairs ahead
-    f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 s, dp;  // chains start from -lse2 / -delta
     auto rd = [&](const char* t, int ks) {
       return *reinterpret_cast<const bf16x8*>(t + st.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
     };
@@ -408,7 +417,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], ks == 0 ? st.neglse2 : s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[ks & 1], st.dof[ks], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[ks & 1], st.dof[ks], ks == 0 ? st.negdelta : dp, 0, 0, 0);
       if (ks + 2 < 8) {
         fk[ks & 1] = rd(ktile, ks + 2);
         fv[ks & 1] = rd(vtile, ks + 2);
@@ -433,7 +442,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     }
     bf16x8 dsb[2];
 #pragma unroll
-    for (int ri = 0; ri < 16; ++ri) dsb[ri >> 3][ri & 7] = (__bf16)(pv[ri] * (dp[ri] - st.delta));
+    for (int ri = 0; ri < 16; ++ri) dsb[ri >> 3][ri & 7] = (__bf16)(pv[ri] * dp[ri]);
 
     // dQ^T += K^T dS^T over the two 16-key steps of this half
     auto tr = [&](int i) {  // i = 4 half + db
@@ -479,7 +488,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const float scale_log2 = p.scale_log2;
 
   QWave st;
-  float nl2;  // -lse2 of this lane's query
+  float nl2, nd;  // -lse2 and -delta of this lane's query
   {
     const int qr = qrow < p.nq ? qrow : p.nq - 1;  // rows past nq: computed, never stored
     const int64_t off = (int64_t)qr * p.q_stride + (int64_t)h * D + 8 * hh;
@@ -491,7 +500,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     const bool in_tiles = qrow < p.nqt * QT_ROWS;
     const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qrow;
     nl2 = in_tiles ? p.nlse2[srow] : 0.f;
-    st.delta = in_tiles ? p.delta[srow] : 0.f;
+    nd = in_tiles ? p.ndelta[srow] : 0.f;
     st.qd = in_tiles ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
@@ -527,7 +536,10 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.qf[s8][e] = (__bf16)((float)st.qf[s8][e] * scale_log2);
 #pragma unroll
-  for (int ri = 0; ri < 16; ++ri) st.neglse2[ri] = nl2;
+  for (int ri = 0; ri < 16; ++ri) {
+    st.neglse2[ri] = nl2;
+    st.negdelta[ri] = nd;
+  }
 
   // (always_inline: otherwise the wave state would be passed through scratch)
   auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) __attribute__((always_inline)) {

@@ -102,7 +102,7 @@ struct BwdParams {
   const uint16_t *q, *k, *v, *o, *d_o;  // [T][H][128] bf16 (q, o, d_o: q_stride; k, v: kv_stride)
   const float* lse;        // [H][nq], natural log (from the forward)
   uint16_t *dq, *dk, *dv;  // outputs, same layouts as q / k / v
-  float* delta;            // workspace [H][nqt*128]: rowsum(dO * O)
+  float* ndelta;           // workspace [H][nqt*128]: -rowsum(dO * O)
   float* nlse2;            // workspace [H][nqt*128]: -lse * log2(e), 0 where -inf or padding
   const QDescDev* qdesc;   // nqt*128 entries
   const KDescDev* kdesc;   // nkt*64 entries

@@ -181,7 +181,7 @@ def test_host_only_plan_cannot_run_and_cache_checks():
 
 def test_backward_entry_checks_on_host_plans():
     """The backward refuses host-only plans and reports its workspace: two fp32
-    row statistics (delta, -lse * log2 e) per head and padded query row."""
+    row statistics (-delta, -lse * log2 e) per head and padded query row."""
     a = seg()
     b = seg(index=1)
     p = host_plan([a, b], [a, b], heads=3)
