@@ -47,26 +47,31 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 
 
+# Every source the forward launch is compiled from or scheduled by: the
+# kernels, their shared device helpers and interface, the C ABI that fills the
+# launch parameters, and the host plan that builds the schedule.
+FWD_SOURCES = ("attn_fwd.hip", "tile_common.h", "kernels.h", "abi.cpp", "plan.cpp", "plan.h")
+TRAFFIC_PROFILE = os.path.join("profiles", "attn_fwd_480p_cached_step_traffic.json")
+
+
 def kernel_hash():
-    """Hash of the sources that decide the forward's HBM traffic (kernel and
-    host schedule)."""
+    """Hash of the sources that decide the forward's HBM traffic."""
     h = hashlib.sha256()
-    for f in ("attn_fwd.hip", "plan.cpp"):
+    for f in FWD_SOURCES:
         h.update(open(os.path.join(ROOT, "segment_causal_masked_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload):
-    """HBM bytes per forward launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "attn_fwd_480p_cached_step_traffic.json")
+    """(HBM bytes per forward launch, source) from the committed counter
+    summary if it was taken on the current forward sources; else (None, None)."""
     try:
-        d = json.load(open(path))
+        d = json.load(open(os.path.join(ROOT, TRAFFIC_PROFILE)))
     except (OSError, ValueError):
-        return None
+        return None, None
     if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return None, None
+    return d.get("hbm_bytes_per_launch"), "profile:" + TRAFFIC_PROFILE
 
 
 def cpu_model():
@@ -79,7 +84,7 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, runs=3):
+def cpu_baseline(w, runs=3, full=True):
     """The fp64 oracle (numpy, BLAS threads = this process's cores) on one full
     forward call of the same workload -- all 16 heads, every query of the new
     segment against all cached + new keys -- median of `runs` runs."""
@@ -111,14 +116,16 @@ def cpu_baseline(w, runs=3):
             "kind": "oracle",
             "sample": f"one forward call of {w.name} ({w.heads} heads, {w.n_q} queries x "
                       f"{w.n_keys} keys), fp64 numpy, median of {runs} runs: {dt:.2f} s",
-            "cpu": cpu_model(), "blas": blas, "other_workloads": cpu_other_workloads()}
+            "cpu": cpu_model(), "blas": blas, "other_workloads": cpu_other_workloads(full)}
 
 
-def cpu_other_workloads():
-    """The oracle on the other forward shapes, for context: the single 480p
-    segment in full (one run) and a 256-query sample of one 720p long-session
-    call (all 16 heads, every key), scaled to the whole call by its share of
-    the unmasked pairs."""
+def cpu_other_workloads(full=True):
+    """The oracle on the other shapes, for context: the single 480p segment in
+    full (one run); one 720p long-session call in full (one run, all 16 heads,
+    rows in blocks of 512; with full=False a 256-query sample scaled by its
+    share of the unmasked pairs); and the training pack's forward and
+    backward for the 4,096-token slice the GPU tests check (every query of
+    its video that sees those keys, 2 heads, one run)."""
     import oracle
     from segment_causal_masked_amd import workloads as wl
     out = {}
@@ -133,19 +140,72 @@ def cpu_other_workloads():
     w = wl.long_session_720p()
     keys = w.cached + w.new
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
-    rows = np.arange(w.n_q - 256, w.n_q)  # the last 256 queries (video, head and tail tokens)
     kc, vc = w.cache_kv()
     k = np.concatenate([kc, w.k_new()])
     v = np.concatenate([vc, w.v_new()])
-    t0 = time.perf_counter()
-    oracle.forward(w.q(), k, v, tq, tk, 128 ** -0.5, rows=rows)
-    dt = time.perf_counter() - t0
-    a_rows = oracle.unmasked_pairs(tq.take(rows), tk)
     a_all = oracle.unmasked_pairs(tq, tk)
-    out["long_session_720p"] = {"seconds_sample": round(dt, 3), "seconds_per_call_scaled": round(dt * a_all / a_rows, 1),
-                                "tflops": round(4.0 * 128 * w.heads * a_rows / dt / 1e12, 6),
-                                "sample": "256 of 7,232 queries, all keys and heads, one run"}
+    if full:
+        t0 = time.perf_counter()
+        oracle.forward(w.q(), k, v, tq, tk, 128 ** -0.5)
+        dt = time.perf_counter() - t0
+        out["long_session_720p"] = {"seconds": round(dt, 2),
+                                    "tflops": round(4.0 * 128 * w.heads * a_all / dt / 1e12, 6),
+                                    "sample": "one whole call (7,232 queries x 122,944 keys, 16 heads), "
+                                              "rows in blocks of 512, one run"}
+    else:
+        rows = np.arange(w.n_q - 256, w.n_q)  # the last 256 queries (video, head and tail tokens)
+        t0 = time.perf_counter()
+        oracle.forward(w.q(), k, v, tq, tk, 128 ** -0.5, rows=rows)
+        dt = time.perf_counter() - t0
+        a_rows = oracle.unmasked_pairs(tq.take(rows), tk)
+        out["long_session_720p"] = {"seconds_sample": round(dt, 3),
+                                    "seconds_per_call_scaled": round(dt * a_all / a_rows, 1),
+                                    "tflops": round(4.0 * 128 * w.heads * a_rows / dt / 1e12, 6),
+                                    "sample": "256 of 7,232 queries, all keys and heads, one run"}
+    # training pack: the 4,096-token slice starting 2,048 tokens before video
+    # 1's third segment; forward for its rows, backward for its dQ rows and
+    # dK / dV rows (which needs every query of video 1)
+    w = wl.training_pack_131k()
+    segs = w.q_layout
+    starts = np.cumsum([0] + [s.n_tokens for s in segs])
+    v1 = [i for i, s in enumerate(segs) if s.video == 1]
+    t_lo, t_hi = int(starts[v1[0]]), int(starts[v1[-1] + 1])
+    rows = np.arange(int(starts[v1[2]]) - 2048, int(starts[v1[2]]) + 2048) - t_lo
+    t = oracle.expand(segs[v1[0]:v1[-1] + 1])
+    heads = [2, 11]
+    vs = slice(t_lo, t_hi)
+    q, k, v, d_o = w.q()[vs], w.k_new()[vs], w.v_new()[vs], w.d_o()[vs]
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, t, t, 128 ** -0.5, rows=rows, heads=heads)
+    t1 = time.perf_counter()
+    oracle.backward(q, k, v, d_o, t, t, 128 ** -0.5, heads=heads, q_rows=rows, k_rows=rows)
+    t2 = time.perf_counter()
+    a_video = oracle.unmasked_pairs(t, t)
+    out["training_pack_slice"] = {"fwd_seconds": round(t1 - t0, 2), "bwd_seconds": round(t2 - t1, 2),
+                                  "video_tokens": int(t_hi - t_lo), "heads": len(heads),
+                                  "bwd_tflops_8DHA": round(8.0 * 128 * len(heads) * a_video / (t2 - t1) / 1e12, 6),
+                                  "sample": "4,096-token slice of video 1 (forward rows; backward over "
+                                            "every query of video 1), 2 heads, one run"}
     return out
+
+
+def mfma_probe(torch, iters=20000):
+    """The MFMA throughput probe (segment_causal_masked_amd/probe): dense bf16
+    TFLOP/s of back-to-back v_mfma_f32_32x32x16_bf16 with no memory traffic
+    and the shader clock meanwhile (the practical ceiling of the roofline)."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "segment_causal_masked_amd", "libnomas_probe.so"))
+    lib.nomas_probe_mfma.restype = C.c_int
+    lib.nomas_probe_mfma.argtypes = [C.c_int] + [C.POINTER(C.c_double)] * 3
+    tf, mhz, ms = C.c_double(), C.c_double(), C.c_double()
+    rc = lib.nomas_probe_mfma(iters, C.byref(tf), C.byref(mhz), C.byref(ms))
+    if rc != 0:
+        return {"error": f"hip error {rc}"}
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    at_clock = cus * mhz.value * 1e6 * 4096 / 1e12
+    return {"tflops": round(tf.value, 1), "clock_mhz": round(mhz.value, 1), "ms": round(ms.value, 3),
+            "cus": cus, "peak_at_clock_tflops": round(at_clock, 1),
+            "frac_of_published_peak": round(tf.value / PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
@@ -372,6 +432,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-quick", action="store_true",
+                    help="oracle context rows on samples only (a 256-query part of the 720p "
+                         "call instead of the whole call)")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the extra forward + backward row on the 131072-token pack")
     ap.add_argument("--no-long-session", action="store_true",
@@ -479,6 +542,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    probe = mfma_probe(torch)       # untimed: the chip's MFMA ceiling and clock
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -532,7 +597,7 @@ def main():
     value = flop_call * NFE * L / (ms_step * 1e-3) / 1e12
     fwd_avg = float(fwd_ms.mean())
     achieved = flop_call / (fwd_avg * 1e-3) / 1e12
-    traffic = traffic_from_profiles(w.name)
+    traffic, traffic_source = traffic_from_profiles(w.name)
     app_bytes = 2 * 2 * w.n_new * H * D * 2  # K and V, read + write
     line = {
         "metric": "effective TFLOP/s of action-aware causal attn fwd; % of bf16 MFMA peak",
@@ -556,7 +621,11 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # counters cannot be read inside this run (they need the
+                     # profiler): the figure, when present, is the committed one
+                     # taken on the same forward sources
+                     "traffic_source": traffic_source},
         "fwd_ms_per_call": round(fwd_avg, 4),
         "fwd_ms_median": round(float(np.median(fwd_ms)), 4),
         "fwd_calls_timed": int(fwd_ms.size),
@@ -566,6 +635,7 @@ def main():
         "append_gbs": round(app_bytes / (float(app_ms.mean()) * 1e-3) / 1e9, 1),
         "plan_host_ms": round(plan_ms, 3),
         "kernel_sha": kernel_hash(),
+        "mfma_probe": probe,
     }
     if sparse_row is not None:
         line["sparse_step"] = sparse_row
@@ -592,7 +662,7 @@ def main():
     if not args.no_camera:
         line["camera_xattn"] = bench_camera(nm, wl, torch)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"] = cpu_baseline(w, full=not args.cpu_quick)
     print(json.dumps(line), flush=True)
 
 

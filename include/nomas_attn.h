@@ -28,10 +28,11 @@
  * Conventions for every call:
  *   - every function returns a nomas_status and never aborts or throws; on
  *     failure nomas_last_error() holds a thread-local description;
- *   - Q, K, V, O, dO, dQ, dK, dV are bf16, token-major [tokens][heads][128]
- *     with the 128 dims contiguous and a caller-given token stride (elements,
- *     >= heads*128, multiple of 8, at most 2^24: larger ones return
- *     INVALID_ARGUMENT); device pointers must be 16-byte aligned;
+ *   - Q, K, V, O, dO, dQ, dK, dV are bf16 (dQ, dK, dV fp32 on request),
+ *     token-major [tokens][heads][128] with the 128 dims contiguous and a
+ *     caller-given token stride (elements, >= heads*128, multiple of 8, at
+ *     most 2^24: larger ones return INVALID_ARGUMENT); device pointers must
+ *     be 16-byte aligned;
  *   - LSE is fp32 [heads][queries] (natural log; -inf for a row that sees no
  *     key);
  *   - device work is enqueued on the caller's HIP stream (NULL = default
@@ -109,8 +110,11 @@ enum { NOMAS_TEXT_QUERY_R = 0, NOMAS_TEXT_QUERY_K = 1, NOMAS_TEXT_QUERY_H = 2 };
 
 /* Plan flags. */
 enum {
-  NOMAS_PLAN_HOST_ONLY = 1 /* build host tables only (no device upload);
-                              such a plan cannot run nomas_attn_fwd/bwd */
+  NOMAS_PLAN_HOST_ONLY = 1, /* build host tables only (no device upload);
+                               such a plan cannot run nomas_attn_fwd/bwd */
+  NOMAS_PLAN_GRAD_F32 = 2   /* nomas_attn_bwd writes dq, dk, dv as fp32
+                               (same layouts and element strides as the
+                               bf16 gradients); without it they are bf16 */
 };
 
 typedef struct {
@@ -138,15 +142,21 @@ typedef struct {
                               pages keep 25% of video blocks after the first
                               two denoising steps ("Summary (Overview)",
                               Inference) without stating the selection; the
-                              score taken is, in fp32, the dot product of the
-                              unit's query sum and the tile's key sum:
+                              score taken is the dot product of the unit's
+                              query sum and the tile's key sum,
                               s = sum_d (sum_q Q[q,d]) * (sum_k K[k,d]),
-                              with separately rounded adds and products; a
-                              row sum adds groups of 16 consecutive rows
-                              (each in ascending order) in ascending group
-                              order, from +0.0; the dot runs over ascending
-                              d; ties go to the lower key tile.  Forward
-                              only.                                        */
+                              i.e. the sum of the unit's logits over the
+                              tile (up to the softmax scale); ties go to the
+                              lower key tile.  The library evaluates s in
+                              fp32 (row sums in groups of 16 rows, then the
+                              group sums; products and adds rounded
+                              separately; ascending d), deterministically, so
+                              its ranking can differ from the exact one only
+                              between tiles whose scores lie within that
+                              evaluation's rounding error of each other.  A
+                              unit's list may hold at most 4096 key tiles
+                              (262,144 keys); longer ones make the plan
+                              return UNSUPPORTED.  Forward only.          */
 } nomas_plan_opts;
 
 typedef struct nomas_plan nomas_plan;
@@ -245,11 +255,15 @@ nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* plan, size_t* bytes
 /* Gradients of O = attention(Q, K, V) for upstream dO:
  *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
  *   dK = scale dS^T Q,
- * with P recomputed from lse (which must come from nomas_attn_fwd on the same
- * inputs).  q, o, d_o, dq share q_stride; k, v, dk, dv share kv_stride.
- * dq, dk, dv are written (not accumulated), bf16.
+ * (the calculus of the softmax attention defined above) with P recomputed as
+ * exp(scale * (Q K^T) - lse) from Q and K as given and lse from
+ * nomas_attn_fwd on the same inputs.  q, o, d_o, dq share q_stride; k, v, dk,
+ * dv share kv_stride (elements).  dq, dk, dv are written (not accumulated):
+ * bf16, or fp32 if the plan was built with NOMAS_PLAN_GRAD_F32.  The work is
+ * deterministic (no atomics): equal inputs give bit-identical gradients.
  * Errors: INVALID_ARGUMENT (plan with a cache, host-only plan, missing
- * pointer or workspace), ALIGNMENT, HIP. */
+ * pointer or workspace), UNSUPPORTED (video-block sparse plan), ALIGNMENT,
+ * HIP. */
 nomas_status nomas_attn_bwd(const nomas_plan* plan,
                             const void* q, const void* k, const void* v,
                             const void* o, const void* d_o, const float* lse,

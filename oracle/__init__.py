@@ -39,7 +39,8 @@ choice, never hidden):
   * rows with no visible key (padding) give O = 0 and LSE = -inf.
   * sliding window (optional, mask.py rule 8): whole segments.
   * video-block sparsity (optional, sparse.py): which blocks are kept is
-    stated there (pooled-sum block score in fp32, ties to the lower tile).
+    stated there (the exact dot product of a query unit's sum and a key
+    tile's sum, ties to the lower tile; geometry given as parameters).
   * camera cross-attention (camera.py, [Summary] Camera-Trajectory
     Conditioning, Eq. 3): one camera token per latent frame, a video query
     sees its own segment's camera tokens within a frame radius (all of them

@@ -32,13 +32,18 @@ def _f64(x):
 
 
 def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
-            rows=None, heads=None, block=512, window=0, tile_keep=None):
+            rows=None, heads=None, block=512, window=0, tile_keep=None, unit_rows=None,
+            tile_keys=None):
     """O [len(rows), Hs, D] and LSE [Hs, len(rows)] (natural log), fp64.
 
     rows: query indices to evaluate (default all); heads: head indices.
-    tile_keep: optional bool [H, query pairs, key tiles] (sparse.select_tiles):
-    key tile t is hidden from the queries of pair u in head h where False.
+    tile_keep: optional bool [H, query units, key tiles] (sparse.select_tiles,
+    with the same unit_rows and tile_keys): key tile t (keys tile_keys * t
+    onward) is hidden from the queries of unit u (rows unit_rows * u onward)
+    in head h where False.
     """
+    if tile_keep is not None and (unit_rows is None or tile_keys is None):
+        raise ValueError("tile_keep needs unit_rows and tile_keys")
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     heads = list(range(q.shape[1])) if heads is None else list(heads)
@@ -49,7 +54,7 @@ def forward(q, k, v, tq: TokenAttrs, tk: TokenAttrs, scale: float, mode="R",
         m0 = visible_mask(tq.take(ridx), tk, mode, window)
         for hi, h in enumerate(heads):
             m = m0 if tile_keep is None else \
-                m0 & tile_keep[h][ridx // 256][:, np.arange(k.shape[0]) // 64]
+                m0 & tile_keep[h][ridx // unit_rows][:, np.arange(k.shape[0]) // tile_keys]
             any_vis = m.any(axis=1)
             s = scale * (q[ridx, h, :] @ k[:, h, :].T)
             s = np.where(m, s, -np.inf)

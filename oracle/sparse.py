@@ -1,107 +1,98 @@
-"""Video-block sparse attention (oracle side).
+"""Video-block sparse attention (oracle side).  TEST INFRASTRUCTURE ONLY.
 
 [Summary] Inference: after the first two denoising steps only a quarter of
 the video blocks are retained.  The pages leave the selection open; the
 reading followed (the same one the library states at its boundary):
 
-  * blocks are 64-key tiles; a video block is a key tile whose keys are all
-    video tokens; tiles holding any head, tail or padding key are always
-    kept;
-  * per (head h, query-tile pair u) -- queries 256 u .. 256 u + 255 -- the
-    candidates are the video tiles that some query of u can see at all, and
-    the ceil(P% of them) with the highest block score are kept;
-  * block score, in float32 with every product and add rounded on its own:
-        qsum[d] = sum over rows r = 0..255 of Q[256 u + r, h, d],
-        ksum[d] = sum over rows r = 0..63 of K[64 t + r, h, d],
-        s       = sum over d = 0..127 of qsum[d] * ksum[d], ascending d,
-    where a row sum is taken in groups of 16 consecutive rows -- each group
-    added in ascending row order, then the group sums in ascending group
-    order, every sum starting from +0.0 -- and rows past the end enter as
-    +0.0;
+  * a block is a key tile of `tile_keys` consecutive keys; a video block is a
+    tile whose keys are all video tokens; a tile holding any head, tail or
+    padding key is always kept;
+  * selection is made per (head h, query unit u), a unit being `unit_rows`
+    consecutive queries; u's candidates are the video tiles that some query
+    of u can see at all, and the ceil(P% of them) with the highest block
+    score are kept;
+  * block score: the dot product of the unit's query sum and the tile's key
+    sum,
+        s(h, u, t) = sum_d (sum_{q in u} Q[q, h, d]) * (sum_{k in t} K[k, h, d]),
+    which equals the sum of all the unit's query-key logits over the tile
+    (bilinearity);
   * ties go to the lower tile index.
 
-The selection is a decision taken in floating point, so it is stated in the
-precision the device takes it in (fp32) and in a fixed order of operations.
-The attention itself is then the plain masked softmax of attention.forward
-with the dropped tiles hidden (tile_keep).
+Here the score is evaluated exactly (fp64, whose sums of bf16 values are exact
+at these sizes).  The attention itself is the plain masked softmax of
+attention.forward with the dropped tiles hidden (its tile_keep argument).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .tiles import tile_classes
+from .mask import visible_mask
 from .tokens import V, TokenAttrs
 
-BQ_PAIR, BK = 256, 64
 
-
-def video_tiles(tk: TokenAttrs, bk: int = BK) -> np.ndarray:
+def video_tiles(tk: TokenAttrs, tile_keys: int) -> np.ndarray:
     """bool per key tile: every key in it is a video token."""
     nk = len(tk)
-    nkt = -(-nk // bk)
+    nkt = -(-nk // tile_keys)
     out = np.zeros(nkt, bool)
     for t in range(nkt):
-        out[t] = bool((tk.kind[t * bk:(t + 1) * bk] == V).all())
+        out[t] = bool((tk.kind[t * tile_keys:(t + 1) * tile_keys] == V).all())
     return out
 
 
-GROUP = 16
-
-
-def _f32_block_sums(x: np.ndarray, rows: int) -> np.ndarray:
-    """x [n, H, D] -> float32 [ceil(n / rows), H, D]: the sum of each block of
-    `rows` consecutive rows in the stated order -- groups of GROUP rows, each
-    added in ascending row order, then the group sums in ascending order,
-    every sum from +0.0 with one rounding per add; rows past the end enter
-    as +0.0."""
+def block_sums(x, rows: int) -> np.ndarray:
+    """x [n, H, D] -> fp64 [ceil(n / rows), H, D]: sums of consecutive blocks
+    of `rows` rows (the last block may be short)."""
+    x = np.asarray(x, np.float64)
     n = x.shape[0]
     nb = -(-n // rows)
-    xp = np.zeros((nb * rows,) + x.shape[1:], np.float32)
-    xp[:n] = np.asarray(x, np.float32)
-    xp = xp.reshape((nb, rows // GROUP, GROUP) + x.shape[1:])
-    part = np.zeros((nb, rows // GROUP) + x.shape[1:], np.float32)
-    for r in range(GROUP):
-        part = (part + xp[:, :, r]).astype(np.float32)
-    acc = np.zeros((nb,) + x.shape[1:], np.float32)
-    for g in range(rows // GROUP):
-        acc = (acc + part[:, g]).astype(np.float32)
-    return acc
+    out = np.zeros((nb,) + x.shape[1:])
+    for b in range(nb):
+        out[b] = x[b * rows:(b + 1) * rows].sum(axis=0)
+    return out
 
 
-def block_scores(q, k) -> np.ndarray:
-    """float32 s[h, u, t] for every head, query pair u and key tile t."""
-    qsum = _f32_block_sums(q, BQ_PAIR)        # [n_pairs, H, D]
-    ksum = _f32_block_sums(k, BK)             # [nkt, H, D]
-    qs = np.transpose(qsum, (1, 0, 2))        # [H, n_pairs, D]
-    ks = np.transpose(ksum, (1, 0, 2))        # [H, nkt, D]
-    s = np.zeros((qs.shape[0], qs.shape[1], ks.shape[1]), np.float32)
-    for d in range(qs.shape[2]):
-        prod = (qs[:, :, None, d] * ks[:, None, :, d]).astype(np.float32)
-        s = (s + prod).astype(np.float32)
-    return s
+def block_scores(q, k, unit_rows: int, tile_keys: int) -> np.ndarray:
+    """fp64 s[h, u, t] for every head, query unit u and key tile t."""
+    qs = block_sums(q, unit_rows)     # [n_units, H, D]
+    ks = block_sums(k, tile_keys)     # [n_tiles, H, D]
+    return np.einsum("uhd,thd->hut", qs, ks)
 
 
-def select_tiles(q, k, tq: TokenAttrs, tk: TokenAttrs, keep_percent: int, mode="R",
-                 heads=None, window=0) -> np.ndarray:
-    """bool keep[h, u, t]: key tile t is attended by query pair u in head h.
+def candidates(tq: TokenAttrs, tk: TokenAttrs, unit_rows: int, tile_keys: int, mode="R",
+               window=0) -> np.ndarray:
+    """bool seen[u, t]: some query of unit u sees some key of tile t."""
+    nq, nk = len(tq), len(tk)
+    n_units, nkt = -(-nq // unit_rows), -(-nk // tile_keys)
+    seen = np.zeros((n_units, nkt), bool)
+    for u in range(n_units):
+        m = visible_mask(tq.take(np.arange(u * unit_rows, min(nq, (u + 1) * unit_rows))), tk,
+                         mode, window)
+        cols = m.any(axis=0)
+        seen[u] = np.logical_or.reduceat(cols, np.arange(0, nk, tile_keys)) if nk else seen[u]
+    return seen
 
-    Non-video tiles are always True; of each pair's candidate video tiles the
-    ceil(keep_percent% of them) best-scoring ones are True.
+
+def select_tiles(q, k, tq: TokenAttrs, tk: TokenAttrs, keep_percent: int, unit_rows: int,
+                 tile_keys: int, mode="R", heads=None, window=0) -> np.ndarray:
+    """bool keep[h, u, t]: key tile t is attended by query unit u in head h.
+
+    Tiles that are not video tiles are always True; of each unit's candidate
+    video tiles the ceil(keep_percent% of them) best-scoring are True (ties:
+    lower tile first); the other video tiles are False.
     """
     nq, nk = len(tq), len(tk)
-    n_pairs = -(-nq // BQ_PAIR)
-    nkt = -(-nk // BK)
+    n_units, nkt = -(-nq // unit_rows), -(-nk // tile_keys)
     heads = list(range(q.shape[1])) if heads is None else list(heads)
-    vid = video_tiles(tk)
-    cls = tile_classes(tq, tk, 128, BK, mode, window=window)
-    scores = block_scores(q, k)
-    keep = np.ones((q.shape[1], n_pairs, nkt), bool)
-    for u in range(n_pairs):
-        seen = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
-        cand = [t for t in range(nkt) if seen[t] and vid[t]]
+    vid = video_tiles(tk, tile_keys)
+    seen = candidates(tq, tk, unit_rows, tile_keys, mode, window)
+    scores = block_scores(q, k, unit_rows, tile_keys)
+    keep = np.ones((q.shape[1], n_units, nkt), bool)
+    for u in range(n_units):
+        cand = [t for t in range(nkt) if seen[u, t] and vid[t]]
         n_keep = -(-len(cand) * keep_percent // 100)
         for h in heads:
             keep[h, u, vid] = False
-            order = sorted(cand, key=lambda t: (-float(scores[h, u, t]), t))
+            order = sorted(cand, key=lambda t: (-scores[h, u, t], t))
             keep[h, u, order[:n_keep]] = True
     return keep

@@ -22,6 +22,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_STALE_P
     ERR_ALIGNMENT, ERR_HIP = range(8)
 TEXT_QUERY = {"R": 0, "K": 1, "H": 2}
 PLAN_HOST_ONLY = 1
+PLAN_GRAD_F32 = 2
 TILE_EMPTY, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 
 
@@ -190,9 +191,10 @@ def _token_stride(t, name, heads):
 # ----------------------------------------------------------------------------
 
 class Plan:
-    def __init__(self, handle, heads):
+    def __init__(self, handle, heads, grad_f32=False):
         self.handle = C.c_void_p(handle)
         self.heads = heads
+        self.grad_f32 = grad_f32
 
     def info(self) -> nomas_plan_info:
         return nomas_plan_get_info(self)
@@ -251,16 +253,17 @@ class KVCache:
 # ----------------------------------------------------------------------------
 
 def nomas_attn_plan(q_layout, kv_layout, cache=None, *, heads=16, mode="R", host_only=False,
-                    block_q=0, block_k=0, window=0, video_keep_percent=0) -> Plan:
+                    block_q=0, block_k=0, window=0, video_keep_percent=0, grad_f32=False) -> Plan:
     lib = load()
     ql, kl = _Layout(q_layout), _Layout(kv_layout)
-    opts = nomas_plan_opts(heads, HEAD_DIM, block_q, block_k, TEXT_QUERY[mode],
-                           PLAN_HOST_ONLY if host_only else 0, window, video_keep_percent)
+    flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_GRAD_F32 if grad_f32 else 0)
+    opts = nomas_plan_opts(heads, HEAD_DIM, block_q, block_k, TEXT_QUERY[mode], flags, window,
+                           video_keep_percent)
     out = C.c_void_p()
     _check(lib.nomas_attn_plan(C.byref(ql.c), C.byref(kl.c),
                                cache.handle if cache is not None else None,
                                C.byref(opts), C.byref(out)), "nomas_attn_plan")
-    return Plan(out.value, heads)
+    return Plan(out.value, heads, grad_f32)
 
 
 def nomas_plan_get_info(plan) -> nomas_plan_info:
@@ -317,6 +320,10 @@ def nomas_attn_bwd(plan, q, k, v, o, d_o, lse, dq, dk, dv, scale=HEAD_DIM ** -0.
     for name, t in (("v", v), ("dk", dk), ("dv", dv)):
         if _token_stride(t, name, h) != ks:
             raise ValueError(f"{name} must share k's token stride")
+    want = "torch.float32" if plan.grad_f32 else "torch.bfloat16"
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None and str(t.dtype) != want:
+            raise ValueError(f"{name} must be {want} for this plan")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().nomas_attn_bwd(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
                                  _ptr(lse), qs, ks, _ptr(dq), _ptr(dk), _ptr(dv), float(scale),

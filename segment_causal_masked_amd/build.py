@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnomas_attn.so")
+# the MFMA throughput probe the benchmark reports beside its roofline (a
+# measuring instrument, built as its own library)
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_peak.hip")
+PROBE_LIB = os.path.join(PKG, "libnomas_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -60,6 +64,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *[o for _, o in jobs]])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *COMMON, *DEVICE, "-shared", PROBE_SRC, "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

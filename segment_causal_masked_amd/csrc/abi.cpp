@@ -510,6 +510,7 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.nkt = (int32_t)h.nkt;
   bp.n_pairs = (int32_t)h.n_pairs;
   bp.n_kpairs = (int32_t)h.n_kpairs;
+  bp.grad_f32 = h.grad_f32 ? 1 : 0;
   bp.scale = scale;
   bp.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = nomas::launch_attn_bwd(bp, static_cast<hipStream_t>(hip_stream));

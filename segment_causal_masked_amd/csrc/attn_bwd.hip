@@ -7,6 +7,14 @@
 //   P = exp(scale S - lse),  dV = P^T dO,  dP = dO V^T,
 //   delta = rowsum(dO * O),  dS = P * (dP - delta),
 //   dQ = scale dS K,  dK = scale dS^T Q.
+// Both gradient kernels form P the same way, from the scores of Q and K as
+// given (bf16 products, fp32 accumulation) scaled by scale * log2(e) in fp32:
+// P = exp2(s * scale * log2(e) - lse * log2(e)).  The forward rounds
+// Q * scale * log2(e) to bf16 before its products, so its lse differs from
+// the exact one by a softmax-weighted mean of those rounding shifts; the rows
+// of this P then sum to exp(-(that difference)) instead of 1, a relative
+// error bounded per row by the forward's LSE bound, and smaller than forming
+// P from the forward's rounded scores would leave against exact gradients.
 // Three launches on one stream:
 //   1. bwd_rowstats_kernel: -delta and -lse * log2(e) per (head, query);
 //   2. bwd_dkdv_kernel: one workgroup per pair of 64-key tiles of a head
@@ -181,8 +189,8 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
     const int b = 2 * qh + bb;
     // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  Hidden pairs
     // start their score chain at -inf and end there: P = 0 (uniform branch,
-    // so FULL tiles skip the selects).  K is not pre-scaled here: the
-    // scores keep the rounding of the forward's, whose lse they meet.
+    // so FULL tiles skip the selects).  Q and K enter unscaled and the fp32
+    // score is scaled once (the P of the dQ kernel, formed the same way).
     // the dP chain starts from -delta of those queries and ends at dP - delta
     f32x16 s = f32x16{}, dp;
 #pragma unroll
@@ -241,16 +249,26 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
   }
 }
 
-// Column of this lane's key: dims 32 db + 8 g + 4 hh + {0..3}.
-__device__ __forceinline__ void kv_store(uint16_t* dst, const f32x16* acc, float mul, int hh) {
+// One lane's gradient row (dims 32 db + 8 g + 4 hh + {0..3}) times mul, as
+// bf16 (RNE) or fp32 elements of row `row` (element offset) of dst.
+template <bool F32>
+__device__ __forceinline__ void store_grad_row(void* dst, int64_t row, const f32x16* acc, float mul,
+                                               int hh) {
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      uint2 pk;
-      pk.x = (uint32_t)f2bf(acc[db][4 * g + 0] * mul) | ((uint32_t)f2bf(acc[db][4 * g + 1] * mul) << 16);
-      pk.y = (uint32_t)f2bf(acc[db][4 * g + 2] * mul) | ((uint32_t)f2bf(acc[db][4 * g + 3] * mul) << 16);
-      *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g + 4 * hh) = pk;
+      const int64_t d0 = row + 32 * db + 8 * g + 4 * hh;
+      const float a0 = acc[db][4 * g + 0] * mul, a1 = acc[db][4 * g + 1] * mul;
+      const float a2 = acc[db][4 * g + 2] * mul, a3 = acc[db][4 * g + 3] * mul;
+      if (F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(dst) + d0) = float4{a0, a1, a2, a3};
+      } else {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+        pk.y = (uint32_t)f2bf(a2) | ((uint32_t)f2bf(a3) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + d0) = pk;
+      }
     }
 }
 
@@ -356,8 +374,13 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     if (key < p.nk) {
       const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * D;
-      kv_store(p.dv + off, st.dv, 1.f, hh);
-      kv_store(p.dk + off, st.dk, p.scale, hh);
+      if (p.grad_f32) {
+        store_grad_row<true>(p.dv, off, st.dv, 1.f, hh);
+        store_grad_row<true>(p.dk, off, st.dk, p.scale, hh);
+      } else {
+        store_grad_row<false>(p.dv, off, st.dv, 1.f, hh);
+        store_grad_row<false>(p.dk, off, st.dk, p.scale, hh);
+      }
     }
   }
 }
@@ -371,12 +394,11 @@ constexpr int Q_THREADS = 64 * Q_WAVES;
 constexpr int Q_STAGE_BYTES = 2 * TILE_BYTES;  // K | V of one 64-key tile
 
 struct QWave {
-  bf16x8 qf[8];    // Q row of this lane's query times scale * log2(e) (bf16, as
-                   // the forward rounds it), dims [16 s + 8 hh, +8)
+  bf16x8 qf[8];    // Q row of this lane's query, dims [16 s + 8 hh, +8)
   bf16x8 dof[8];   // dO row, same layout
   f32x16 acc[4];   // dQ^T (unscaled), dims 32 db + 8 (ri / 4) + 4 hh + ri % 4
   f32x16 negdelta;  // -delta in every register: the dP chains start from it
-  f32x16 neglse2;   // -lse2 in every register: the score chains start from it
+  float nlse2;      // -lse * log2(e) of this lane's query
   QDescDev qd;
   int kbase[2];    // K / V row-read base for even / odd 16-dim steps
   int tbase[2];    // K transpose-read base for rows +0 / +4
@@ -395,15 +417,15 @@ __device__ __forceinline__ uint32_t dq_vis_bits(const QDescDev& qd, const KDescD
   return v;
 }
 
-// With Q pre-scaled and the score chain started from -lse2, the accumulator
-// holds s * scale * log2(e) - lse2: P = exp2 of it, as in the forward.
+// P = exp2(s * scale * log2(e) - lse2) from the fp32 score of Q and K as
+// given, as the dK/dV kernel forms it.
 __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char* vtile, bool masked,
-                                        uint32_t vis, int hh) {
+                                        uint32_t vis, float scale_log2, int hh) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     // S^T and dP^T for keys 32 kb + (0..31): two chains, interleaved, with the
     // K / V row fragments read two MFMA pairs ahead
-    f32x16 s, dp;  // chains start from -lse2 / -delta
+    f32x16 s, dp;  // chains start from 0 / -delta
     auto rd = [&](const char* t, int ks) {
       return *reinterpret_cast<const bf16x8*>(t + st.kbase[ks & 1] + 2048 * kb + 4096 * (ks >> 1));
     };
@@ -416,7 +438,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     __builtin_amdgcn_s_setprio(1);  // as the forward's S^T block
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], ks == 0 ? st.neglse2 : s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[ks & 1], st.qf[ks], ks == 0 ? f32x16{} : s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv[ks & 1], st.dof[ks], ks == 0 ? st.negdelta : dp, 0, 0, 0);
       if (ks + 2 < 8) {
         fk[ks & 1] = rd(ktile, ks + 2);
@@ -435,7 +457,7 @@ __device__ __forceinline__ void dq_tile(QWave& st, const char* ktile, const char
     // register ri holds key 32 kb + 16 (ri / 8) + 8 hh + ri % 8
     float pv[16];
 #pragma unroll
-    for (int ri = 0; ri < 16; ++ri) pv[ri] = __builtin_amdgcn_exp2f(s[ri]);
+    for (int ri = 0; ri < 16; ++ri) pv[ri] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ri], scale_log2, st.nlse2));
     if (masked) {  // uniform: PARTIAL (or ragged) tiles only
 #pragma unroll
       for (int ri = 0; ri < 16; ++ri) pv[ri] = ((vis >> (16 * kb + ri)) & 1u) ? pv[ri] : 0.f;
@@ -530,16 +552,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
   const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
   wait_vm_all();  // rows and statistics in registers before the tile loads start
-  // Q * scale * log2(e) rounded to bf16, as the forward formed its scores
+  st.nlse2 = nl2;
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.qf[s8][e] = (__bf16)((float)st.qf[s8][e] * scale_log2);
-#pragma unroll
-  for (int ri = 0; ri < 16; ++ri) {
-    st.neglse2[ri] = nl2;
-    st.negdelta[ri] = nd;
-  }
+  for (int ri = 0; ri < 16; ++ri) st.negdelta[ri] = nd;
 
   // (always_inline: otherwise the wave state would be passed through scratch)
   auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) __attribute__((always_inline)) {
@@ -554,7 +569,7 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     // uniform branch that FULL tiles skip
     const bool masked = (here >> half) & 1;
     const uint32_t vis = masked ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
-    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, hh);
+    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, scale_log2, hh);
   };
   // four stages used as two pairs, one barrier per pair (as in the forward)
   auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
@@ -579,18 +594,9 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   }
 
   if (qrow < p.nq) {
-    uint16_t* dst = p.dq + (int64_t)qrow * p.q_stride + (int64_t)h * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(st.acc[db][4 * g + 0] * p.scale) |
-               ((uint32_t)f2bf(st.acc[db][4 * g + 1] * p.scale) << 16);
-        pk.y = (uint32_t)f2bf(st.acc[db][4 * g + 2] * p.scale) |
-               ((uint32_t)f2bf(st.acc[db][4 * g + 3] * p.scale) << 16);
-        *reinterpret_cast<uint2*>(dst + 32 * db + 8 * g + 4 * hh) = pk;
-      }
+    const int64_t off = (int64_t)qrow * p.q_stride + (int64_t)h * D;
+    if (p.grad_f32) store_grad_row<true>(p.dq, off, st.acc, p.scale, hh);
+    else store_grad_row<false>(p.dq, off, st.acc, p.scale, hh);
   }
 }
 

@@ -101,7 +101,8 @@ hipError_t launch_kvcache_int8_expand(const Int8ExpandParams& p, hipStream_t str
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *d_o;  // [T][H][128] bf16 (q, o, d_o: q_stride; k, v: kv_stride)
   const float* lse;        // [H][nq], natural log (from the forward)
-  uint16_t *dq, *dk, *dv;  // outputs, same layouts as q / k / v
+  uint16_t *dq, *dk, *dv;  // outputs, same layouts (element strides) as q / k / v;
+                           // fp32 elements when grad_f32 != 0, else bf16
   float* ndelta;           // workspace [H][nqt*128]: -rowsum(dO * O)
   float* nlse2;            // workspace [H][nqt*128]: -lse * log2(e), 0 where -inf or padding
   const QDescDev* qdesc;   // nqt*128 entries
@@ -110,6 +111,7 @@ struct BwdParams {
   const int32_t *kpair_ptr, *kpair_idx;  // per key-tile pair: (q_tile << 4) | flags
   int64_t q_stride, kv_stride;
   int32_t nq, nk, heads, nqt, nkt, n_pairs, n_kpairs;
+  int32_t grad_f32;
   float scale, scale_log2;
 };
 

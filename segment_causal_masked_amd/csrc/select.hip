@@ -5,14 +5,21 @@
 // are chosen; the reading implemented here (and stated in the ABI header):
 // per (head h, query-tile pair u), among the key tiles of u's list whose keys
 // are all video tokens, keep the ceil(P% of them) with the highest block score
-//     s(h, u, t) = sum_d qsum[d] * ksum[d]   (ascending d),
+//     s(h, u, t) = sum_d qsum[d] * ksum[d],
 //     qsum[d] = sum of Q[q, h, d] over the 256 query rows of u,
 //     ksum[d] = sum of K[k, h, d] over the 64 key rows of tile t,
-// every add and product rounded separately in fp32; a row sum is taken in
-// groups of 16 consecutive rows -- each group summed in ascending row order,
-// then the group sums added in ascending group order, every sum starting from
-// +0.0 -- and rows past the end enter as +0.0; ties go to the lower key tile.  Tiles holding any head, tail or padding key
-// are always kept.  The kept entries, in list order, form u's list for head h.
+// (the sum of u's logits over tile t, up to the softmax scale); ties go to
+// the lower key tile.  Tiles holding any head, tail or padding key are always
+// kept.  The kept entries, in list order, form u's list for head h.
+//
+// s is evaluated in fp32 in a fixed order, so the lists are deterministic:
+// every add and product rounded separately (this file is built without
+// floating-point contraction), a row sum taken in groups of 16 consecutive
+// rows -- each group summed in ascending row order, then the group sums added
+// in ascending group order, every sum starting from +0.0, rows past the end
+// entering as +0.0 -- and the dot over ascending d.  The ranking then differs
+// from the exact one only between tiles whose exact scores are closer than
+// the rounding error of that evaluation.
 //
 // Three launches: key-tile sums, query-pair sums, then one workgroup per
 // (pair, head) that scores, sorts (bitonic, in LDS) and compacts the list.

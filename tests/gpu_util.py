@@ -5,17 +5,17 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import segment_causal_masked_amd as nm
+import tolerance as tol
 
 SCALE = 128 ** -0.5
 
 # Parity gate of the attention output: max-abs 1e-2 and mean-abs 1e-3 on
-# unit-scale outputs (inputs ~ N(0,1)).  LSE: the forward multiplies Q by
-# scale * log2(e) and rounds it to bf16 before the products, which moves a
-# score by at most 2^-9 * scale * sum_d |q_d k_d| (about 82 for N(0,1)
-# inputs: <= 1.4e-2 in natural-log units, ~1e-3 typical); the LSE, a soft
-# maximum of the scores, moves by a weighted mean of those shifts.  Gate 5e-3.
-O_MAX_ABS, O_MEAN_ABS, LSE_ABS = 1e-2, 1e-3, 5e-3
+# unit-scale outputs (inputs ~ N(0,1)).  LSE: a per-row bound derived from the
+# device's roundings (tolerance.lse_bound): the forward rounds Q * scale *
+# log2(e) to bf16 before its products.
+O_MAX_ABS, O_MEAN_ABS = 1e-2, 1e-3
 
 
 def need_gpu():
@@ -46,14 +46,27 @@ def check_o(o_gpu, o_ref, what=""):
     assert np.isfinite(o_gpu).all()
 
 
-def check_lse(lse_gpu, lse_ref, what=""):
+def oracle_forward(q, k, v, tq, tk, scale=SCALE, u_inputs=0.0, **kw):
+    """The oracle's (O, LSE) and the device LSE bound for the same rows and
+    heads (kw as oracle.forward)."""
+    o_ref, l_ref = oracle.forward(q, k, v, tq, tk, scale, **kw)
+    bkw = {n: kw[n] for n in ("mode", "rows", "heads", "window", "tile_keep", "unit_rows",
+                              "tile_keys") if n in kw}
+    return o_ref, l_ref, tol.lse_bound(q, k, tq, tk, scale, u_inputs=u_inputs, **bkw)
+
+
+def check_lse(lse_gpu, lse_ref, what, bound):
+    """Rows that see no key: -inf exactly; others within their derived bound."""
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_gpu), fin), what
     assert np.all(lse_gpu[~fin] == -np.inf)
     if fin.any():
-        d = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max())
-        say(f"  {what}: LSE max-abs {d:.3e}")
-        assert d <= LSE_ABS, (what, d)
+        d = np.abs(lse_gpu[fin] - lse_ref[fin])
+        b = bound[fin]
+        r = float((d / b).max())
+        say(f"  {what}: LSE max-abs {float(d.max()):.3e}, max err/bound {r:.3f} "
+            f"(bound median {float(np.median(b)):.2e})")
+        assert r <= 1.0, (what, r)
 
 
 def new_cache(heads, capacity):

@@ -252,12 +252,14 @@ def test_plan_sparse_list_lengths_match_oracle(keep):
     q = w.q()[:, :1]
     kc, _ = w.cache_kv()
     k = np.concatenate([kc, w.k_new()])[:, :1]
-    kept = sparse.select_tiles(q, k, tq, tk, keep)
+    kept = sparse.select_tiles(q, k, tq, tk, keep, unit_rows=256, tile_keys=64)
+    seen = sparse.candidates(tq, tk, 256, 64) | ~sparse.video_tiles(tk, 64)[None, :]
     cls = oracle.tile_classes(tq, tk, 128, 64)
     total = 0
     for u in range(kept.shape[1]):
-        seen = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
-        total += int((kept[0, u] & seen).sum())
+        in_list = (cls[2 * u] != 0) | ((cls[2 * u + 1] != 0) if 2 * u + 1 < cls.shape[0] else False)
+        assert not (in_list & ~seen[u]).any()
+        total += int((kept[0, u] & in_list).sum())
     assert info.sparse_list_entries == total
 
 

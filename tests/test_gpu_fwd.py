@@ -7,7 +7,7 @@ import torch
 import oracle
 import segment_causal_masked_amd as nm
 from segment_causal_masked_amd import workloads as wl
-from gpu_util import (SCALE, check_lse, check_o, dev, fill_cache, host, need_gpu, new_cache,
+from gpu_util import (SCALE, check_lse, oracle_forward, check_o, dev, fill_cache, host, need_gpu, new_cache,
                       run_fwd, say, stored_rows)
 
 pytestmark = pytest.mark.gpu
@@ -27,9 +27,11 @@ def dense_case(w, mode="R", nfe=0):
     return plan, q, k, v, keys
 
 
-def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None, window=0):
+def oracle_fwd(w, q, k, v, keys, mode="R", rows=None, heads=None, window=0, u_inputs=0.0):
+    """(O, LSE) of the oracle and the LSE bound of the device for those rows."""
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
-    return oracle.forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads, window=window)
+    return oracle_forward(q, k, v, tq, tk, SCALE, mode=mode, rows=rows, heads=heads, window=window,
+                          u_inputs=u_inputs)
 
 
 def test_tiny_two_segments_fp32_inputs():
@@ -38,13 +40,14 @@ def test_tiny_two_segments_fp32_inputs():
     say("tiny two segments: 96 tokens, 1 head, fp32 inputs rounded to bf16 for the kernel")
     plan, q, k, v, keys = dense_case(w)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 1)
-    o_ref, l_ref = oracle_fwd(w, q, k, v, keys)            # oracle on the fp32 inputs
+    # oracle on the fp32 inputs: the LSE bound adds the kernel's bf16 rounding of Q and K
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, k, v, keys, u_inputs=2.0 ** -8)
     check_o(host(o), o_ref, "vs fp32 inputs")
-    check_lse(host(l), l_ref, "vs fp32 inputs")
+    check_lse(host(l), l_ref, "vs fp32 inputs", l_bnd)
     qb, kb, vb = (wl.round_to_bf16(x) for x in (q, k, v))
-    o_ref_b, l_ref_b = oracle_fwd(w, qb, kb, vb, keys)     # same bf16 values
+    o_ref_b, l_ref_b, l_bnd_b = oracle_fwd(w, qb, kb, vb, keys)     # same bf16 values
     check_o(host(o), o_ref_b, "vs bf16 inputs")
-    check_lse(host(l), l_ref_b, "vs bf16 inputs")
+    check_lse(host(l), l_ref_b, "vs bf16 inputs", l_bnd_b)
 
 
 @pytest.mark.parametrize("mode", ["R", "K", "H"])
@@ -55,10 +58,10 @@ def test_single_segment_480p(mode):
     plan, q, k, v, keys = dense_case(w, mode)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     heads = None if mode == "R" else [0, 7, 15]
-    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, mode=mode, heads=heads)
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, k, v, keys, mode=mode, heads=heads)
     hsel = slice(None) if heads is None else heads
     check_o(host(o)[:, hsel], o_ref, f"single segment {mode}")
-    check_lse(host(l)[hsel], l_ref, f"single segment {mode}")
+    check_lse(host(l)[hsel], l_ref, f"single segment {mode}", l_bnd)
 
 
 def test_single_segment_480p_sorted_windows():
@@ -66,9 +69,9 @@ def test_single_segment_480p_sorted_windows():
     w = wl.single_segment_480p(seed_set=1)
     plan, q, k, v, keys = dense_case(w)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
-    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, heads=[3, 12])
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, k, v, keys, heads=[3, 12])
     check_o(host(o)[:, [3, 12]], o_ref, "single segment, sorted windows")
-    check_lse(host(l)[[3, 12]], l_ref, "single segment, sorted windows")
+    check_lse(host(l)[[3, 12]], l_ref, "single segment, sorted windows", l_bnd)
 
 
 def build_cached(w, layer=0):
@@ -99,9 +102,9 @@ def test_cached_step_480p_and_append_layout():
     q, kn, vn = w.q(), w.k_new(), w.v_new()
     o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
     keys = w.cached + w.new
-    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys)
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys)
     check_o(host(o), o_ref, "480p cached step")
-    check_lse(host(l), l_ref, "480p cached step")
+    check_lse(host(l), l_ref, "480p cached step", l_bnd)
 
 
 def test_cached_step_equals_full_sequence_bitwise():
@@ -168,9 +171,9 @@ def test_padding_rows_and_ragged_shapes():
     plan = nm.nomas_attn_plan(segs, segs, heads=3)
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 3)
     t = oracle.expand(segs)
-    o_ref, l_ref = oracle.forward(q, k, v, t, t, SCALE)
+    o_ref, l_ref, l_bnd = oracle_forward(q, k, v, t, t, SCALE)
     check_o(host(o), o_ref, "ragged pack")
-    check_lse(host(l), l_ref, "ragged pack")
+    check_lse(host(l), l_ref, "ragged pack", l_bnd)
     pad = t.kind == oracle.PAD
     assert (host(o)[pad] == 0).all()
 
@@ -197,9 +200,9 @@ def test_thirty_two_actions_and_many_cached_segments():
     o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 2)
     keys = cached + [big]
     tq, tk = oracle.expand([big]), oracle.expand(keys)
-    o_ref, l_ref = oracle.forward(q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), tq, tk, SCALE)
+    o_ref, l_ref, l_bnd = oracle_forward(q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), tq, tk, SCALE)
     check_o(host(o), o_ref, "32 actions, 40 cached segments")
-    check_lse(host(l), l_ref, "32 actions, 40 cached segments")
+    check_lse(host(l), l_ref, "32 actions, 40 cached segments", l_bnd)
 
 
 def test_single_token_and_empty_query():
@@ -261,10 +264,10 @@ def test_long_session_720p_sampled_rows():
     for nfe in range(4):
         q, kn, vn = w.q(nfe), w.k_new(nfe), w.v_new(nfe)
         o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
-        o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+        o_ref, l_ref, l_bnd = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
                                   rows=rows, heads=heads)
         check_o(host(o)[rows][:, heads], o_ref, f"720p long session call {nfe}")
-        check_lse(host(l)[heads][:, rows], l_ref, f"720p long session call {nfe}")
+        check_lse(host(l)[heads][:, rows], l_ref, f"720p long session call {nfe}", l_bnd)
     nm.nomas_kvcache_append(cache, w.new[0], dev(kn), dev(vn))   # K/V of the last call
     torch.cuda.synchronize()
     n_old, n_add = len(stored_rows(w.cached)), len(stored_rows(w.new))
@@ -294,10 +297,10 @@ def test_long_session_720p_two_heads_split_units():
     rows = np.sort(np.concatenate([g.choice(w.n_q, 48, replace=False),
                                    np.arange(w.n_q - 256, w.n_q, 29)]))
     keys = w.cached + w.new
-    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
                               rows=rows)
     check_o(host(o)[rows], o_ref, "720p, 2 heads")
-    check_lse(host(l)[:, rows], l_ref, "720p, 2 heads")
+    check_lse(host(l)[:, rows], l_ref, "720p, 2 heads", l_bnd)
 
 
 @pytest.mark.parametrize("window", [1, 2])
@@ -313,10 +316,10 @@ def test_cached_step_480p_sliding_window(window):
     q, kn, vn = w.q(), w.k_new(), w.v_new()
     o, l = run_fwd(plan, cache, dev(q), dev(kn), dev(vn), 16)
     keys = w.cached + w.new
-    o_ref, l_ref = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, np.concatenate([kc, kn]), np.concatenate([vc, vn]), keys,
                               heads=[1, 14], window=window)
     check_o(host(o)[:, [1, 14]], o_ref, f"window {window}")
-    check_lse(host(l)[[1, 14]], l_ref, f"window {window}")
+    check_lse(host(l)[[1, 14]], l_ref, f"window {window}", l_bnd)
 
 
 def test_training_pack_131k_forward_sampled():
@@ -327,6 +330,6 @@ def test_training_pack_131k_forward_sampled():
     o, l = run_fwd(plan, None, dev(q), dev(k), dev(v), 16)
     g = np.random.default_rng(55)
     rows = np.sort(g.choice(w.n_q, 48, replace=False))
-    o_ref, l_ref = oracle_fwd(w, q, k, v, keys, rows=rows, heads=[0, 13])
+    o_ref, l_ref, l_bnd = oracle_fwd(w, q, k, v, keys, rows=rows, heads=[0, 13])
     check_o(host(o)[rows][:, [0, 13]], o_ref, "training pack fwd")
-    check_lse(host(l)[[0, 13]][:, rows], l_ref, "training pack fwd")
+    check_lse(host(l)[[0, 13]][:, rows], l_ref, "training pack fwd", l_bnd)
