@@ -246,6 +246,26 @@ nomas_status nomas_attn_fwd(const nomas_plan* plan, const nomas_kvcache* cache,
                             void* workspace, size_t workspace_bytes,
                             void* hip_stream);
 
+/* The same forward for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: no workspace argument, and the call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine).  Its workspace is a
+ * fixed device array of the library, 64 MiB (NOMAS_NOALLOC_SCRATCH_BYTES),
+ * which each device the library runs on holds until the process ends (its
+ * address is resolved when a plan is first built on that device).  Results
+ * are those of nomas_attn_fwd, bit for bit.  Every call on a device shares
+ * that device's array, so calls that overlap on one device (concurrent
+ * streams, threads) race; serialise them.  A plan whose
+ * nomas_attn_fwd_workspace_size exceeds the array is rejected with
+ * UNSUPPORTED before anything is enqueued.
+ * Errors: as nomas_attn_fwd, and UNSUPPORTED (workspace above 64 MiB). */
+#define NOMAS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+nomas_status nomas_attn_fwd_noalloc(const nomas_plan* plan, const nomas_kvcache* cache,
+                                    const void* q, int64_t q_stride,
+                                    const void* k_new, const void* v_new, int64_t kv_stride,
+                                    void* o, int64_t o_stride, float* lse, float scale,
+                                    void* hip_stream);
+
 /* --------------------------------------------------------------------------
  * Backward (plans without a cache: training packs)
  * ------------------------------------------------------------------------ */

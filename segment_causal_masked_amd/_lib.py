@@ -91,6 +91,7 @@ def load():
         "nomas_plan_destroy": [P],
         "nomas_attn_fwd_workspace_size": [P, C.POINTER(SZ)],
         "nomas_attn_fwd": [P, P, P, I64, P, P, I64, P, I64, P, F32, P, SZ, P],
+        "nomas_attn_fwd_noalloc": [P, P, P, I64, P, P, I64, P, I64, P, F32, P],
         "nomas_attn_bwd_workspace_size": [P, C.POINTER(SZ)],
         "nomas_attn_bwd": [P, P, P, P, P, P, P, I64, I64, P, P, P, F32, P, SZ, P],
         "nomas_kvcache_create": [I32, I32, I64, P, P, C.POINTER(P)],
@@ -301,6 +302,21 @@ def nomas_attn_fwd(plan, cache, q, k_new, v_new, o, lse=None, scale=HEAD_DIM ** 
                                  _ptr(q), qs, _ptr(k_new), _ptr(v_new), ks, _ptr(o), os_,
                                  _ptr(lse), float(scale), _ptr(workspace), ws_bytes,
                                  _stream_ptr(stream, q)), "nomas_attn_fwd")
+
+
+def nomas_attn_fwd_noalloc(plan, cache, q, k_new, v_new, o, lse=None, scale=HEAD_DIM ** -0.5,
+                           stream=None):
+    h = plan.heads
+    qs = _token_stride(q, "q", h)
+    os_ = _token_stride(o, "o", h)
+    ks = _token_stride(k_new, "k_new", h)
+    vs = _token_stride(v_new, "v_new", h)
+    if k_new is not None and v_new is not None and ks != vs:
+        raise ValueError("k_new and v_new must share a token stride")
+    _check(load().nomas_attn_fwd_noalloc(plan.handle, cache.handle if cache is not None else None,
+                                         _ptr(q), qs, _ptr(k_new), _ptr(v_new), ks, _ptr(o), os_,
+                                         _ptr(lse), float(scale), _stream_ptr(stream, q)),
+           "nomas_attn_fwd_noalloc")
 
 
 def nomas_attn_bwd_workspace_size(plan) -> int:

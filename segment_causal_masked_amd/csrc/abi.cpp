@@ -191,6 +191,14 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
       return hip_fail(e, "device query");
     }
     groups = cus * nomas::attn_fwd_groups_per_cu();
+    // set-up of the allocation-free forward on this device: its scratch
+    // address, resolved once per device while the device is current
+    void* scratch = nullptr;
+    e = nomas::noalloc_scratch(p->device, &scratch);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "device scratch address");
+    }
   }
   nomas::build_fwd_schedule(&p->host, groups);
   if (p->host.keep_percent > 0) {
@@ -346,17 +354,26 @@ nomas_status nomas_attn_fwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   return ok();
 }
 
-nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, const void* q,
-                            int64_t q_stride, const void* k_new, const void* v_new,
-                            int64_t kv_stride, void* o, int64_t o_stride, float* lse,
-                            float scale, void* workspace, size_t workspace_bytes,
-                            void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+nomas_status check_fwd_plan(const nomas_plan* p, const nomas_kvcache* cache) {
   if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!p->on_device) return fail(NOMAS_ERR_INVALID_ARGUMENT, "host-only plan cannot run");
   if (!plan_matches_cache(p, cache))
     return fail(p->has_cache && cache ? NOMAS_ERR_STALE_PLAN : NOMAS_ERR_INVALID_ARGUMENT,
                 p->has_cache && cache ? "cache changed since the plan was built"
                                       : "cache argument does not match the plan");
+  return NOMAS_OK;
+}
+
+// The forward of a checked plan over `workspace` (device memory of at least
+// the plan's workspace size): argument checks and launches, no allocation.
+nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const void* q,
+                      int64_t q_stride, const void* k_new, const void* v_new, int64_t kv_stride,
+                      void* o, int64_t o_stride, float* lse, float scale, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
   const nomas::HostPlan& h = p->host;
   const bool has_new = h.nk > h.n_cached;
   nomas_status s;
@@ -443,6 +460,41 @@ nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, con
   hipError_t e = nomas::launch_attn_fwd(fp, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+nomas_status nomas_attn_fwd(const nomas_plan* p, const nomas_kvcache* cache, const void* q,
+                            int64_t q_stride, const void* k_new, const void* v_new,
+                            int64_t kv_stride, void* o, int64_t o_stride, float* lse,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            void* hip_stream) {
+  nomas_status s = check_fwd_plan(p, cache);
+  if (s != NOMAS_OK) return s;
+  return fwd_impl(p, cache, q, q_stride, k_new, v_new, kv_stride, o, o_stride, lse, scale,
+                  workspace, workspace_bytes, hip_stream);
+}
+
+nomas_status nomas_attn_fwd_noalloc(const nomas_plan* p, const nomas_kvcache* cache,
+                                    const void* q, int64_t q_stride, const void* k_new,
+                                    const void* v_new, int64_t kv_stride, void* o,
+                                    int64_t o_stride, float* lse, float scale, void* hip_stream) {
+  nomas_status s = check_fwd_plan(p, cache);
+  if (s != NOMAS_OK) return s;
+  const size_t need = fwd_workspace(p->host).total;
+  if (need > nomas::NOALLOC_SCRATCH_BYTES)
+    return fail(NOMAS_ERR_UNSUPPORTED,
+                "plan needs " + std::to_string(need) + " bytes of forward workspace; "
+                "nomas_attn_fwd_noalloc holds at most " +
+                    std::to_string(nomas::NOALLOC_SCRATCH_BYTES) + " (use nomas_attn_fwd)");
+  if ((s = check_device(p))) return s;
+  void* scratch = nullptr;
+  hipError_t e = nomas::noalloc_scratch(p->device, &scratch);
+  if (e != hipSuccess) return hip_fail(e, "device scratch address");
+  return fwd_impl(p, cache, q, q_stride, k_new, v_new, kv_stride, o, o_stride, lse, scale,
+                  need ? scratch : nullptr, need ? nomas::NOALLOC_SCRATCH_BYTES : 0, hip_stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -43,6 +43,12 @@ struct FwdParams {
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream);
 
+// Fixed device scratch of the allocation-free forward (noalloc.hip): its
+// address on `device` (which must be the current device on the first call for
+// it), resolved once per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
+
 // Video-block selection of sparse plans (select.hip): per (head, query-tile
 // pair) the kept key-tile list, written to `lists`.
 struct SelParams {
