@@ -320,6 +320,20 @@ nomas_status nomas_kvcache_append(nomas_kvcache* cache, const nomas_segment* seg
  * cache held exactly those segments become valid again. */
 nomas_status nomas_kvcache_truncate(nomas_kvcache* cache, int32_t n_segments);
 
+/* Resume a cache: an empty handle (just created, or reset) takes on the
+ * segments whose rows are already in its buffers -- written by appends to a
+ * cache over the same buffers, or saved and restored by the caller -- in
+ * append order, segment i's stored rows (video and head tokens) following
+ * those of segments 0 .. i-1 from row 0 of every head.  Nothing is copied or
+ * launched; plans built for these segments are valid with it.  The pages'
+ * cache is permanent and grows segment by segment ("One World, Generated
+ * Segment by Segment"); this lets a session continue in a new process.
+ * Errors: INVALID_ARGUMENT (NULL, cache not empty), LAYOUT (malformed record,
+ * a segment listed twice), CAPACITY (rows beyond capacity); on error nothing
+ * is recorded. */
+nomas_status nomas_kvcache_adopt(nomas_kvcache* cache, const nomas_segment* segments,
+                                 int32_t n_segments);
+
 nomas_status nomas_kvcache_reset(nomas_kvcache* cache);
 /* n_tokens: stored rows (video + head tokens of the cached segments). */
 nomas_status nomas_kvcache_len(const nomas_kvcache* cache, int64_t* n_tokens,
@@ -366,6 +380,11 @@ nomas_status nomas_kvcache_int8_append(nomas_kvcache_int8* cache, const nomas_se
  * small; nothing written), HIP. */
 nomas_status nomas_kvcache_int8_expand(const nomas_kvcache_int8* cache, nomas_kvcache* dst,
                                        void* hip_stream);
+
+/* As nomas_kvcache_adopt, for codes and exponents already in an INT8
+ * cache's buffers. */
+nomas_status nomas_kvcache_int8_adopt(nomas_kvcache_int8* cache, const nomas_segment* segments,
+                                      int32_t n_segments);
 
 nomas_status nomas_kvcache_int8_truncate(nomas_kvcache_int8* cache, int32_t n_segments);
 nomas_status nomas_kvcache_int8_len(const nomas_kvcache_int8* cache, int64_t* n_tokens,

@@ -7,7 +7,7 @@ library; the first call does, and fails loudly if it is not built.
 """
 from ._lib import (  # noqa: F401
     CameraPlan, KVCache, KVCacheInt8, NomasError, Plan, load,
-    nomas_kvcache_int8_append, nomas_kvcache_int8_create, nomas_kvcache_int8_destroy,
+    nomas_kvcache_adopt, nomas_kvcache_int8_adopt, nomas_kvcache_int8_append, nomas_kvcache_int8_create, nomas_kvcache_int8_destroy,
     nomas_kvcache_int8_expand, nomas_kvcache_int8_len, nomas_kvcache_int8_truncate,
     nomas_camera_attn_fwd, nomas_camera_attn_plan, nomas_camera_plan_destroy,
     nomas_camera_plan_export_ranges, nomas_camera_plan_get_info,

@@ -104,6 +104,8 @@ def load():
         "nomas_kvcache_int8_append": [P, C.POINTER(nomas_segment), P, P, I64, P],
         "nomas_kvcache_int8_expand": [P, P, P],
         "nomas_kvcache_int8_truncate": [P, I32],
+        "nomas_kvcache_adopt": [P, C.POINTER(nomas_segment), I32],
+        "nomas_kvcache_int8_adopt": [P, C.POINTER(nomas_segment), I32],
         "nomas_kvcache_int8_len": [P, C.POINTER(I64), C.POINTER(I32)],
         "nomas_kvcache_int8_destroy": [P],
         "nomas_camera_attn_plan": [C.POINTER(nomas_layout), I32, I32, I32, C.POINTER(P)],
@@ -370,6 +372,12 @@ def nomas_kvcache_truncate(cache, n_segments):
     _check(load().nomas_kvcache_truncate(cache.handle, n_segments), "nomas_kvcache_truncate")
 
 
+def nomas_kvcache_adopt(cache, segments):
+    lay = _Layout(segments)
+    _check(load().nomas_kvcache_adopt(cache.handle, lay.c.segments, lay.c.n_segments),
+           "nomas_kvcache_adopt")
+
+
 def nomas_kvcache_reset(cache):
     _check(load().nomas_kvcache_reset(cache.handle), "nomas_kvcache_reset")
 
@@ -380,13 +388,21 @@ def nomas_kvcache_len(cache):
     return n.value, s.value
 
 
-def nomas_kvcache_int8_create(heads, capacity, device="cuda") -> KVCacheInt8:
-    """Allocates the int8 storage (torch tensors) and creates the handle."""
+def nomas_kvcache_int8_create(heads, capacity, device="cuda", buffers=None) -> KVCacheInt8:
+    """Allocates the int8 storage (torch tensors) and creates the handle;
+    buffers=(k_codes, v_codes, k_exp, v_exp) uses existing storage instead."""
     import torch
-    kc = torch.zeros((heads, capacity, HEAD_DIM), dtype=torch.int8, device=device)
-    vc = torch.zeros_like(kc)
-    ke = torch.zeros((heads, capacity), dtype=torch.int8, device=device)
-    ve = torch.zeros_like(ke)
+    if buffers is None:
+        kc = torch.zeros((heads, capacity, HEAD_DIM), dtype=torch.int8, device=device)
+        vc = torch.zeros_like(kc)
+        ke = torch.zeros((heads, capacity), dtype=torch.int8, device=device)
+        ve = torch.zeros_like(ke)
+    else:
+        kc, vc, ke, ve = buffers
+        for t, shape in ((kc, (heads, capacity, HEAD_DIM)), (vc, (heads, capacity, HEAD_DIM)),
+                         (ke, (heads, capacity)), (ve, (heads, capacity))):
+            if tuple(t.shape) != shape or not t.is_contiguous() or str(t.dtype) != "torch.int8":
+                raise ValueError(f"INT8 cache buffers must be contiguous int8 {shape}")
     out = C.c_void_p()
     _check(load().nomas_kvcache_int8_create(heads, HEAD_DIM, capacity, _ptr(kc), _ptr(vc), _ptr(ke),
                                             _ptr(ve), C.byref(out)), "nomas_kvcache_int8_create")
@@ -409,6 +425,12 @@ def nomas_kvcache_int8_expand(cache, dst, stream=None):
 
 def nomas_kvcache_int8_truncate(cache, n_segments):
     _check(load().nomas_kvcache_int8_truncate(cache.handle, n_segments), "nomas_kvcache_int8_truncate")
+
+
+def nomas_kvcache_int8_adopt(cache, segments):
+    lay = _Layout(segments)
+    _check(load().nomas_kvcache_int8_adopt(cache.handle, lay.c.segments, lay.c.n_segments),
+           "nomas_kvcache_int8_adopt")
 
 
 def nomas_kvcache_int8_len(cache):

@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <chrono>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -30,6 +32,25 @@ nomas_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Environment switches, read once per process:
+//   NOMAS_TRACE=1         one line of plan statistics on stderr per plan;
+//   NOMAS_DEBUG_CHECKS=1  every plan's tables are checked against their
+//                         invariants, and every call waits for its kernels and
+//                         reports a failed one as NOMAS_ERR_HIP (slow: for
+//                         debugging only; not usable under graph capture).
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+bool trace_on() {
+  static const bool on = env_flag("NOMAS_TRACE");
+  return on;
+}
+bool debug_checks() {
+  static const bool on = env_flag("NOMAS_DEBUG_CHECKS");
+  return on;
+}
 
 }  // namespace
 
@@ -90,9 +111,22 @@ nomas_status hip_fail(hipError_t e, const char* where) {
   return fail(NOMAS_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// Under NOMAS_DEBUG_CHECKS: wait for the work just enqueued and report a
+// kernel that failed, naming the call.
+nomas_status debug_sync(void* stream, const char* where) {
+  if (!debug_checks()) return NOMAS_OK;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(NOMAS_ERR_HIP, std::string(where) + " (NOMAS_DEBUG_CHECKS): " +
+                                                      hipGetErrorString(e));
+  return NOMAS_OK;
+}
+
 // A plan encodes the layout only: it is valid for any cache of its head count
 // that holds exactly the segments it was built for (same identities and
 // records, same order), whichever cache object that is.
+size_t fwd_workspace_bytes(const nomas::HostPlan& h);  // defined with the forward
+
 bool plan_matches_cache(const nomas_plan* p, const nomas_kvcache* c) {
   if (!p->has_cache) return c == nullptr;
   if (!c || c->heads != p->host.heads || c->segs.size() != p->cache_segs.size()) return false;
@@ -162,6 +196,7 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
   if (cache && cache->heads != opts->num_heads)
     return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache heads differ from opts.num_heads");
 
+  const auto t_start = std::chrono::steady_clock::now();
   nomas_plan* p = new (std::nothrow) nomas_plan();
   if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, "out of host memory");
   std::string err;
@@ -210,6 +245,13 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
       }
   }
   if (!p->has_cache) nomas::build_bwd_schedule(&p->host);
+  if (debug_checks()) {
+    const std::string bad = nomas::validate_host_plan(p->host);
+    if (!bad.empty()) {
+      delete p;
+      return fail(NOMAS_ERR_INVALID_ARGUMENT, "internal " + bad);
+    }
+  }
   if (!(opts->flags & NOMAS_PLAN_HOST_ONLY)) {
     const nomas::HostPlan& h = p->host;
     struct Part { const void* src; size_t bytes; size_t off; };
@@ -268,6 +310,22 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     p->d_sp_keep = reinterpret_cast<const int32_t*>(base + parts[15].off);
     p->d_video_tile = reinterpret_cast<const int32_t*>(base + parts[16].off);
     p->on_device = true;
+  }
+  if (trace_on()) {
+    const nomas::HostPlan& h = p->host;
+    const double ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t_start).count();
+    std::fprintf(stderr,
+                 "nomas_attn_plan: queries %lld keys %lld (cached %lld) heads %d mode %d window %d "
+                 "keep %d%% | tiles %lldx%lld: full %lld partial %lld empty %lld | A %lld "
+                 "executed/A %.4f | units %lld pieces %zu merges %zu slots %d | fwd workspace %zu B "
+                 "| %s | %.2f ms\n",
+                 (long long)h.nq, (long long)h.nk, (long long)h.n_cached, h.heads, h.mode, h.window,
+                 h.keep_percent, (long long)h.nqt, (long long)h.nkt, (long long)h.n_full,
+                 (long long)h.n_partial, (long long)h.n_empty, (long long)h.unmasked_pairs,
+                 h.unmasked_pairs ? (double)h.executed_pairs / (double)h.unmasked_pairs : 0.0,
+                 (long long)(int64_t(h.heads) * h.n_pairs), h.pieces.size(), h.combine.size(), h.n_slots,
+                 fwd_workspace_bytes(h), p->on_device ? "device" : "host only", ms);
   }
   *out = p;
   return ok();
@@ -343,6 +401,8 @@ FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
   w.total = at;
   return w;
 }
+
+size_t fwd_workspace_bytes(const nomas::HostPlan& h) { return fwd_workspace(h).total; }
 
 }  // namespace
 
@@ -624,6 +684,45 @@ nomas_status nomas_kvcache_append(nomas_kvcache* c, const nomas_segment* seg, co
   c->segs.push_back(*seg);
   c->len += n;
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Records of segments whose rows are already in a cache's buffers: checked
+// like appends (records, duplicates, capacity) before anything is recorded.
+template <typename Cache>
+nomas_status adopt_segments(Cache* c, const nomas_segment* segs, int32_t n) {
+  if (!c) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (n < 0 || (n > 0 && !segs)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "bad segment array");
+  if (!c->segs.empty()) return fail(NOMAS_ERR_INVALID_ARGUMENT, "cache already holds segments");
+  int64_t len = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    std::string e = nomas::check_segment(segs[i]);
+    if (!e.empty()) return fail(NOMAS_ERR_LAYOUT, "segment " + std::to_string(i) + ": " + e);
+    for (int32_t j = 0; j < i; ++j)
+      if (segs[j].video == segs[i].video && segs[j].index == segs[i].index)
+        return fail(NOMAS_ERR_LAYOUT, "segment listed twice");
+    len += nomas::segment_cached_tokens(segs[i]);
+  }
+  if (len > c->capacity) return fail(NOMAS_ERR_CAPACITY, "segments exceed the cache capacity");
+  c->segs.assign(segs, segs + n);
+  c->len = len;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+nomas_status nomas_kvcache_adopt(nomas_kvcache* c, const nomas_segment* segs, int32_t n_segments) {
+  return adopt_segments(c, segs, n_segments);
+}
+
+nomas_status nomas_kvcache_int8_adopt(nomas_kvcache_int8* c, const nomas_segment* segs,
+                                      int32_t n_segments) {
+  return adopt_segments(c, segs, n_segments);
 }
 
 nomas_status nomas_kvcache_truncate(nomas_kvcache* c, int32_t n_segments) {

@@ -484,3 +484,122 @@ void build_bwd_schedule(HostPlan* pp) {
 }
 
 }  // namespace nomas
+
+namespace nomas {
+
+// Consistency of a built plan's tables: the invariants the kernels rely on
+// (indices in range, lists sorted and matching the class map, every unit's
+// iterations covered exactly once by its pieces, slots and merge items
+// consistent).  Returns "" or the first violation.
+std::string validate_host_plan(const HostPlan& p) {
+  auto bad = [](const std::string& what) { return "plan check: " + what; };
+  if (int64_t(p.qdesc.size()) != p.nqt * p.bq || int64_t(p.kdesc.size()) != p.nkt * p.bk)
+    return bad("descriptor array sizes");
+  if (int64_t(p.classes.size()) != p.nqt * p.nkt) return bad("class map size");
+  if (p.nqt != (p.nq + p.bq - 1) / p.bq || p.nkt != (p.nk + p.bk - 1) / p.bk) return bad("tile counts");
+  int64_t cnt[3] = {0, 0, 0};
+  for (uint8_t c : p.classes) {
+    if (c > 2) return bad("class value");
+    ++cnt[c];
+  }
+  if (cnt[NOMAS_TILE_EMPTY] != p.n_empty || cnt[NOMAS_TILE_FULL] != p.n_full ||
+      cnt[NOMAS_TILE_PARTIAL] != p.n_partial)
+    return bad("class counts");
+  if (p.unmasked_pairs < 0 || p.unmasked_pairs > p.executed_pairs || p.executed_pairs > p.nq * p.nk)
+    return bad("pair counts");
+  // CSR (per q-tile) and CSC (per k-tile): ascending non-empty tiles
+  auto check_lists = [&](const std::vector<int32_t>& ptr, const std::vector<int32_t>& idx, int64_t rows,
+                         int64_t cols, bool by_row) -> std::string {
+    if (int64_t(ptr.size()) != rows + 1 || ptr[0] != 0 || ptr.back() != int32_t(idx.size()))
+      return bad(by_row ? "CSR pointers" : "CSC pointers");
+    for (int64_t r = 0; r < rows; ++r) {
+      if (ptr[size_t(r + 1)] < ptr[size_t(r)]) return bad("list pointers not monotone");
+      int64_t n_nonempty = 0;
+      for (int64_t c = 0; c < cols; ++c) {
+        const uint8_t cl = by_row ? p.classes[size_t(r * p.nkt + c)] : p.classes[size_t(c * p.nkt + r)];
+        n_nonempty += cl != NOMAS_TILE_EMPTY;
+      }
+      if (ptr[size_t(r + 1)] - ptr[size_t(r)] != n_nonempty) return bad("list length vs class map");
+      int32_t prev = -1;
+      for (int32_t e = ptr[size_t(r)]; e < ptr[size_t(r + 1)]; ++e) {
+        const int32_t t = idx[size_t(e)] >> 1;
+        if (t <= prev || t >= cols) return bad("list entry out of order or range");
+        const uint8_t cl = by_row ? p.classes[size_t(r * p.nkt + t)] : p.classes[size_t(t * p.nkt + r)];
+        if (cl == NOMAS_TILE_EMPTY) return bad("list holds an EMPTY tile");
+        if (cl == NOMAS_TILE_PARTIAL && !(idx[size_t(e)] & 1)) return bad("PARTIAL tile without mask flag");
+        prev = t;
+      }
+    }
+    return "";
+  };
+  std::string e = check_lists(p.csr_ptr, p.csr_idx, p.nqt, p.nkt, true);
+  if (!e.empty()) return e;
+  e = check_lists(p.csc_ptr, p.csc_idx, p.nkt, p.nqt, false);
+  if (!e.empty()) return e;
+  if (p.pair_ptr.empty()) return "";  // no forward schedule
+  // merged pair lists
+  if (p.n_pairs != (p.nqt + 1) / 2 || int64_t(p.pair_ptr.size()) != p.n_pairs + 1)
+    return bad("pair pointers");
+  for (int64_t u = 0; u < p.n_pairs; ++u) {
+    int32_t prev = -1;
+    for (int32_t i = p.pair_ptr[size_t(u)]; i < p.pair_ptr[size_t(u + 1)]; ++i) {
+      const int32_t v = p.pair_idx[size_t(i)], t = v >> 4;
+      if (t <= prev || t >= p.nkt) return bad("pair entry out of order or range");
+      for (int half = 0; half < 2; ++half) {
+        const int64_t qt = 2 * u + half;
+        const bool empty = qt >= p.nqt || p.classes[size_t(qt * p.nkt + t)] == NOMAS_TILE_EMPTY;
+        if (empty != bool((v >> (2 + half)) & 1)) return bad("pair EMPTY flag vs class map");
+        if (!empty && p.classes[size_t(qt * p.nkt + t)] == NOMAS_TILE_PARTIAL && !((v >> half) & 1))
+          return bad("pair mask flag vs class map");
+      }
+      prev = t;
+    }
+  }
+  const std::vector<int32_t>& lptr = p.keep_percent > 0 ? p.sp_ptr : p.pair_ptr;
+  if (int64_t(lptr.size()) != p.n_pairs + 1) return bad("list pointers of the schedule");
+  // pieces: every unit's entries [0, n) covered exactly once; slots and merges
+  const int64_t n_units = int64_t(p.heads) * p.n_pairs;
+  if (int64_t(p.wg_ptr.size()) != int64_t(p.fwd_groups) + 1 || p.wg_ptr[0] != 0 ||
+      p.wg_ptr.back() != int32_t(p.pieces.size()))
+    return bad("workgroup pointers");
+  for (int32_t g = 0; g < p.fwd_groups; ++g)
+    if (p.wg_ptr[size_t(g + 1)] < p.wg_ptr[size_t(g)]) return bad("workgroup pointers not monotone");
+  std::vector<int64_t> covered(size_t(n_units), 0);
+  std::vector<int32_t> n_pieces(size_t(n_units), 0), n_slotted(size_t(n_units), 0);
+  std::vector<uint8_t> slot_used(size_t(std::max<int32_t>(p.n_slots, 0)), 0);
+  for (const Piece& pc : p.pieces) {
+    if (pc.unit < 0 || pc.unit >= n_units) return bad("piece unit out of range");
+    const int64_t pr = pc.unit % p.n_pairs;
+    const int32_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
+    if (pc.e_begin < 0 || pc.e_begin > pc.e_end || pc.e_end > n) return bad("piece range");
+    covered[size_t(pc.unit)] += pc.e_end - pc.e_begin;
+    ++n_pieces[size_t(pc.unit)];
+    if (pc.slot >= 0) {
+      if (pc.slot >= p.n_slots || slot_used[size_t(pc.slot)]) return bad("piece slot");
+      slot_used[size_t(pc.slot)] = 1;
+      ++n_slotted[size_t(pc.unit)];
+    }
+  }
+  for (int64_t u = 0; u < n_units; ++u) {
+    const int64_t pr = u % p.n_pairs;
+    const int32_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
+    if (covered[size_t(u)] != n || n_pieces[size_t(u)] < 1) return bad("unit not covered exactly once");
+    if ((n_pieces[size_t(u)] > 1) != (n_slotted[size_t(u)] == n_pieces[size_t(u)]) ||
+        (n_pieces[size_t(u)] == 1 && n_slotted[size_t(u)] != 0))
+      return bad("split unit without slots, or slot on a whole unit");
+    if (int64_t(p.unit_shift.size()) != n_units || p.unit_shift[size_t(u)] < 0 ||
+        (n > 0 && p.unit_shift[size_t(u)] >= n))
+      return bad("unit rotation");
+  }
+  int64_t merged = 0;
+  for (const CombineItem& c : p.combine) {
+    if (c.unit < 0 || c.unit >= n_units || c.n_pieces != n_pieces[size_t(c.unit)] || c.n_pieces < 2 ||
+        c.first_slot < 0 || c.first_slot + c.n_pieces > p.n_slots)
+      return bad("merge item");
+    merged += c.n_pieces;
+  }
+  if (merged != p.n_slots) return bad("merge items vs slots");
+  return "";
+}
+
+}  // namespace nomas

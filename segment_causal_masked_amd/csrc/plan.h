@@ -115,6 +115,10 @@ bool same_segment(const nomas_segment& a, const nomas_segment& b);
 // padding to nobody, so no later query can see them.
 int64_t segment_cached_tokens(const nomas_segment& s);
 
+// Invariants of a built plan (lists vs the class map, schedule coverage,
+// slots); "" if they hold, else the first violation.
+std::string validate_host_plan(const HostPlan& p);
+
 // Build the host plan.  keys = cached ++ kv_new.  Returns NOMAS_OK or an
 // error status with *err filled.
 nomas_status build_host_plan(const std::vector<nomas_segment>& q,

@@ -350,3 +350,32 @@ def test_int8_cache_create_rejects_bad_arguments():
     assert lib.nomas_kvcache_int8_len(out, C.byref(n), C.byref(s)) == _lib.OK and (n.value, s.value) == (0, 0)
     assert lib.nomas_kvcache_int8_truncate(out, 1) == _lib.ERR_INVALID_ARGUMENT
     assert lib.nomas_kvcache_int8_destroy(out) == _lib.OK
+
+
+def test_kvcache_adopt_records_existing_rows():
+    """Resume: an empty handle over buffers that already hold rows takes on
+    the segments' records (no copy); errors leave it empty."""
+    lib = _lib.load()
+    segs = wl.cached_step_480p().cached[:2]
+    stored = sum(s.n_frames * s.tokens_per_frame + s.n_head for s in segs)
+    c = C.c_void_p()
+    assert lib.nomas_kvcache_create(2, 128, stored, C.c_void_p(256), C.c_void_p(512), C.byref(c)) == 0
+    cache = nm.KVCache(c.value, None, None, 2, stored)
+    arr = (_lib.nomas_segment * 3)(*[_lib.to_c_segment(s) for s in segs + segs[:1]])
+    # too many rows: CAPACITY, nothing recorded
+    assert lib.nomas_kvcache_adopt(c, arr, 3) in (_lib.ERR_CAPACITY, _lib.ERR_LAYOUT)
+    assert nm.nomas_kvcache_len(cache) == (0, 0)
+    big = (_lib.nomas_segment * 3)(*[_lib.to_c_segment(s) for s in wl.cached_step_480p().cached[:3]])
+    assert lib.nomas_kvcache_adopt(c, big, 3) == _lib.ERR_CAPACITY
+    # a segment listed twice, a malformed record
+    assert lib.nomas_kvcache_adopt(c, (_lib.nomas_segment * 2)(arr[0], arr[0]), 2) == _lib.ERR_LAYOUT
+    broken = _lib.to_c_segment(wl.Segment(0, 5, 2, 16, 8, [(4, 1, 1)]))
+    assert lib.nomas_kvcache_adopt(c, (_lib.nomas_segment * 1)(broken), 1) == _lib.ERR_LAYOUT
+    assert nm.nomas_kvcache_len(cache) == (0, 0)
+    nm.nomas_kvcache_adopt(cache, segs)
+    assert nm.nomas_kvcache_len(cache) == (stored, 2)
+    # not empty any more
+    assert lib.nomas_kvcache_adopt(c, arr, 1) == _lib.ERR_INVALID_ARGUMENT
+    nm.nomas_kvcache_reset(cache)
+    assert lib.nomas_kvcache_adopt(c, arr, 1) == _lib.OK
+    assert lib.nomas_kvcache_adopt(None, arr, 1) == _lib.ERR_INVALID_ARGUMENT

@@ -333,3 +333,59 @@ def test_training_pack_131k_forward_sampled():
     o_ref, l_ref, l_bnd = oracle_fwd(w, q, k, v, keys, rows=rows, heads=[0, 13])
     check_o(host(o)[rows][:, [0, 13]], o_ref, "training pack fwd")
     check_lse(host(l)[[0, 13]][:, rows], l_ref, "training pack fwd", l_bnd)
+
+
+def test_cache_resume_by_adopt_bitwise():
+    """A second handle over the same K/V buffers adopts the cached segments
+    (as a new process would after restoring them): plans of either handle
+    run on either, bit-identical to the forward over the cache that was
+    filled by appends."""
+    need_gpu()
+    w = wl.cached_step_480p()
+    cache, kc, vc = build_cached(w)
+    resumed = nm.nomas_kvcache_create(16, w.n_cached + w.n_new, cache.k_buf, cache.v_buf)
+    nm.nomas_kvcache_adopt(resumed, w.cached)
+    assert nm.nomas_kvcache_len(resumed) == nm.nomas_kvcache_len(cache)
+    q, kn, vn = dev(w.q(1)), dev(w.k_new(1)), dev(w.v_new(1))
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16)
+    plan_r = nm.nomas_attn_plan(w.q_layout, w.new, resumed, heads=16)
+    o1, l1 = run_fwd(plan, cache, q, kn, vn, 16)
+    o2, l2 = run_fwd(plan, resumed, q, kn, vn, 16)
+    o3, l3 = run_fwd(plan_r, resumed, q, kn, vn, 16)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # the resumed cache keeps growing like the original
+    nm.nomas_kvcache_append(resumed, w.new[0], kn, vn)
+    assert nm.nomas_kvcache_len(resumed)[1] == len(w.cached) + 1
+    with pytest.raises(nm.NomasError) as e:
+        nm.nomas_attn_fwd(plan_r, resumed, q, kn, vn, torch.empty_like(q), None, SCALE,
+                          workspace=torch.empty(max(nm.nomas_attn_fwd_workspace_size(plan_r), 16),
+                                                dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 5  # stale plan
+
+
+def test_int8_cache_resume_by_adopt_bitwise():
+    """The same for an INT8 cache: a handle over the same codes adopts the
+    segments, and its expansion equals the original's bit for bit."""
+    need_gpu()
+    w = wl.cached_step_480p()
+    kc, vc = w.cache_kv()
+    cap = w.n_cached + w.n_new
+    c8 = nm.nomas_kvcache_int8_create(16, cap)
+    off = 0
+    kd, vd = dev(kc), dev(vc)
+    for s in w.cached:
+        nm.nomas_kvcache_int8_append(c8, s, kd[off:off + s.n_tokens], vd[off:off + s.n_tokens])
+        off += s.n_tokens
+    r8 = nm.nomas_kvcache_int8_create(16, cap, buffers=(c8.k_codes, c8.v_codes, c8.k_exp, c8.v_exp))
+    nm.nomas_kvcache_int8_adopt(r8, w.cached)
+    works = []
+    for c in (c8, r8):
+        wk = new_cache(16, cap)
+        nm.nomas_kvcache_int8_expand(c, wk)
+        works.append(wk)
+    torch.cuda.synchronize()
+    n = nm.nomas_kvcache_len(works[0])[0]
+    assert nm.nomas_kvcache_len(works[1])[0] == n > 0
+    assert torch.equal(works[0].k_buf[:, :n], works[1].k_buf[:, :n])
+    assert torch.equal(works[0].v_buf[:, :n], works[1].v_buf[:, :n])
