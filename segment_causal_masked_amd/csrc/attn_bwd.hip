@@ -206,15 +206,29 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? 0.f : -INFINITY;
     }
-    // the S / dP chains run at raised priority (as the forward's S^T block)
+    // the S / dP chains run at raised priority (as the forward's S^T block);
+    // their A operands (Q, dO rows) are read one MFMA ahead, so that each
+    // read's latency hides under the previous product instead of stalling it
+    // (two ahead pushes the wave past its registers: K rows spill into the loop)
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    auto afrag = [&](int i) {  // i = 2 ks + (0: Q row, 1: dO row)
+      const int ks = i >> 1;
       const int off = rbase[ks & 1] + 2048 * b + GRP128 * (ks >> 1);
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(qtile + off);
-      const bf16x8 ado = *reinterpret_cast<const bf16x8*>(dotile + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, st.kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, st.vf[ks], dp, 0, 0, 0);
+      return *reinterpret_cast<const bf16x8*>(((i & 1) ? dotile : qtile) + off);
+    };
+    bf16x8 fa = afrag(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 fn = afrag(i + 1 < 16 ? i + 1 : i);
+      if (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, st.vf[i >> 1], dp, 0, 0, 0);
+      else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, st.kf[i >> 1], s, 0, 0, 0);
+      fa = fn;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the first read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // read i + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
     }
     __builtin_amdgcn_s_setprio(0);
     bf16x8 pb[2], dsb[2];
