@@ -386,18 +386,21 @@ def bench_int8_session(nm, wl, torch, sessions=3, warmup=1):
 
 def bench_camera(nm, wl, torch, iters=20, warmup=3):
     """Camera cross-attention (Eq. 3) with every camera token of a segment
-    visible (radius -1): a 480p segment (3,280 tokens, 8 camera tokens) and
-    the 131072-token training pack.  HBM-bound: the figure of merit is the
+    visible (radius -1) and with the time-aligned reading (radius 0: each
+    video token sees its own latent frame's camera token): a 480p segment
+    (3,280 tokens, 8 camera tokens) and the 131072-token training pack.  HBM-bound: the figure of merit is the
     algorithmic bytes (Q and O rows, camera K and V) per call time.  `iters`
     back-to-back calls between two HIP events on the launch stream; the 480p
     case rotates 12 query / output buffer pairs (322 MB, more than the 256 MB
     last-level cache) so that rows come from HBM.  Inputs are drawn on the
     device (timing only)."""
     out = {}
-    for key, w, n_buf in (("segment_480p", wl.single_segment_480p(), 12),
-                          ("training_pack", wl.training_pack_131k(), 1)):
+    for key, w, n_buf, radius in (("segment_480p", wl.single_segment_480p(), 12, -1),
+                                  ("training_pack", wl.training_pack_131k(), 1, -1),
+                                  ("segment_480p_radius0", wl.single_segment_480p(), 12, 0),
+                                  ("training_pack_radius0", wl.training_pack_131k(), 1, 0)):
         H, D = w.heads, 128
-        plan = nm.nomas_camera_attn_plan(w.q_layout, heads=H, radius=-1)
+        plan = nm.nomas_camera_attn_plan(w.q_layout, heads=H, radius=radius)
         info = plan.info()
         g = torch.Generator(device="cuda")
         g.manual_seed(7000)
@@ -417,7 +420,7 @@ def bench_camera(nm, wl, torch, iters=20, warmup=3):
         ms = e0.elapsed_time(e1) / iters
         gbs = info.algorithmic_bytes / (ms * 1e-3) / 1e9
         out[key] = {"workload": w.name, "tokens": w.n_q, "video_tokens": int(info.n_video_queries),
-                    "camera_tokens": int(info.n_camera_tokens), "heads": H, "radius_frames": -1,
+                    "camera_tokens": int(info.n_camera_tokens), "heads": H, "radius_frames": radius,
                     "ms_per_call": round(ms, 4), "algorithmic_mb": round(info.algorithmic_bytes / 1e6, 2),
                     "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                     "effective_tflops": round(info.effective_flop / (ms * 1e-3) / 1e12, 3),

@@ -153,10 +153,11 @@ typedef struct {
                               separately; ascending d), deterministically, so
                               its ranking can differ from the exact one only
                               between tiles whose scores lie within that
-                              evaluation's rounding error of each other.  A
-                              unit's list may hold at most 4096 key tiles
-                              (262,144 keys); longer ones make the plan
-                              return UNSUPPORTED.  Forward only.          */
+                              evaluation's rounding error of each other.
+                              Lists of any length (up to 4096 key tiles are
+                              ranked by a sort in LDS, longer ones by a
+                              radix select; the kept sets are the same).
+                              Forward only.                                */
 } nomas_plan_opts;
 
 typedef struct nomas_plan nomas_plan;

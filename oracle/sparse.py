@@ -43,12 +43,11 @@ def video_tiles(tk: TokenAttrs, tile_keys: int) -> np.ndarray:
 def block_sums(x, rows: int) -> np.ndarray:
     """x [n, H, D] -> fp64 [ceil(n / rows), H, D]: sums of consecutive blocks
     of `rows` rows (the last block may be short)."""
-    x = np.asarray(x, np.float64)
     n = x.shape[0]
     nb = -(-n // rows)
     out = np.zeros((nb,) + x.shape[1:])
     for b in range(nb):
-        out[b] = x[b * rows:(b + 1) * rows].sum(axis=0)
+        out[b] = np.asarray(x[b * rows:(b + 1) * rows], np.float64).sum(axis=0)
     return out
 
 

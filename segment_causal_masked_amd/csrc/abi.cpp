@@ -236,14 +236,6 @@ nomas_status nomas_attn_plan(const nomas_layout* q, const nomas_layout* kv_new,
     }
   }
   nomas::build_fwd_schedule(&p->host, groups);
-  if (p->host.keep_percent > 0) {
-    for (int64_t u = 0; u < p->host.n_pairs; ++u)
-      if (p->host.pair_ptr[size_t(u + 1)] - p->host.pair_ptr[size_t(u)] > nomas::SELECT_MAX_ENTRIES) {
-        delete p;
-        return fail(NOMAS_ERR_UNSUPPORTED, "video_keep_percent: a query-tile pair sees more than " +
-                                               std::to_string(nomas::SELECT_MAX_ENTRIES) + " key tiles");
-      }
-  }
   if (!p->has_cache) nomas::build_bwd_schedule(&p->host);
   if (debug_checks()) {
     const std::string bad = nomas::validate_host_plan(p->host);
@@ -378,10 +370,12 @@ nomas_status nomas_plan_destroy(nomas_plan* p) {
 namespace {
 
 // Forward workspace: [sparse plans: kept lists [H][sp_total] int32 | key sums
-// [H][nkt][128] fp32 | query sums [H][n_pairs][128] fp32] [partial slots],
-// each part 256-byte aligned.
+// [H][nkt][128] fp32 | query sums [H][n_pairs][128] fp32 | (lists longer than
+// 4096 entries) sort keys [H][pair_total] uint64] [partial slots], each part
+// 256-byte aligned.
 struct FwdWorkspace {
-  size_t lists = 0, k_sum = 0, q_sum = 0, partial = 0, total = 0;
+  size_t lists = 0, k_sum = 0, q_sum = 0, keys = 0, partial = 0, total = 0;
+  bool has_keys = false;
 };
 
 FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
@@ -395,6 +389,14 @@ FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
     at += al(size_t(h.heads) * size_t(h.nkt) * 128 * 4);
     w.q_sum = at;
     at += al(size_t(h.heads) * size_t(h.n_pairs) * 128 * 4);
+    // sort keys of the pair lists ranked by radix select (longer than a
+    // workgroup's LDS sort holds)
+    for (int64_t u = 0; u < h.n_pairs && !w.has_keys; ++u)
+      w.has_keys = h.pair_ptr[size_t(u + 1)] - h.pair_ptr[size_t(u)] > nomas::SELECT_SORT_ENTRIES;
+    if (w.has_keys) {
+      w.keys = at;
+      at += al(size_t(h.heads) * size_t(h.pair_ptr.back()) * 8);
+    }
   }
   w.partial = at;
   at += (size_t)h.n_slots * nomas::attn_fwd_slot_bytes();
@@ -465,6 +467,8 @@ nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const voi
     sp.k_sum = reinterpret_cast<float*>(wsb + ws.k_sum);
     sp.q_sum = reinterpret_cast<float*>(wsb + ws.q_sum);
     sp.lists = reinterpret_cast<int32_t*>(wsb + ws.lists);
+    sp.keys = ws.has_keys ? reinterpret_cast<uint64_t*>(wsb + ws.keys) : nullptr;
+    sp.pair_total = h.pair_ptr.back();
     sp.q_stride = q_stride;
     sp.kv_stride = kv_stride;
     sp.cache_cap = cache ? cache->capacity : 0;

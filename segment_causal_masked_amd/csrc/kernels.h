@@ -63,10 +63,14 @@ struct SelParams {
   float* k_sum;             // workspace [H][nkt][128]
   float* q_sum;             // workspace [H][n_pairs][128]
   int32_t* lists;           // workspace [H][sp_total]
-  int64_t q_stride, kv_stride, cache_cap, sp_total;
+  uint64_t* keys;           // workspace [H][pair_total] (null unless some pair list
+                            // is longer than SELECT_SORT_ENTRIES): sort keys of long lists
+  int64_t q_stride, kv_stride, cache_cap, sp_total, pair_total;
   int32_t nq, nk, n_cached, heads, nkt, n_pairs;
 };
-constexpr int SELECT_MAX_ENTRIES = 4096;  // longest pair list a sparse plan may have
+// Pair lists up to this length are ranked by a bitonic sort in LDS; longer
+// ones by a radix select over keys kept in the workspace.
+constexpr int SELECT_SORT_ENTRIES = 4096;
 hipError_t launch_select(const SelParams& p, hipStream_t stream);
 size_t attn_fwd_slot_bytes();
 int attn_fwd_groups_per_cu();  // persistent forward workgroups per CU

@@ -22,7 +22,9 @@
 // the rounding error of that evaluation.
 //
 // Three launches: key-tile sums, query-pair sums, then one workgroup per
-// (pair, head) that scores, sorts (bitonic, in LDS) and compacts the list.
+// (pair, head) that scores, ranks (a bitonic sort in LDS, or for lists of
+// more than 4096 entries a radix select over keys in the workspace) and
+// compacts the list.
 #include "kernels.h"
 
 namespace nomas {
@@ -103,44 +105,128 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Sort key of list entry i (a key tile of the pair's list): (score order <<
+// 32) | ~i, larger = better score, the lower index first among equal scores;
+// 0 for an entry that is not a video tile (always kept, never ranked).
+// Real keys are never 0: order_key of any float is nonzero except for one
+// NaN pattern, and ~i is nonzero for i < 2^32 - 1.
+__device__ __forceinline__ uint64_t entry_key(const SelParams& p, const float* qs, int h, int e0,
+                                              int i) {
+  const int kt = p.pair_idx[e0 + i] >> 4;
+  if (!p.video_tile[kt]) return 0;
+  const float* ks = p.k_sum + ((int64_t)h * p.nkt + kt) * 128;
+  float s = 0.f;
+  // product and sum rounded separately (this file is built without
+  // floating-point contraction), ascending d; loads in batches of 32
+  for (int d0 = 0; d0 < 128; d0 += 32) {
+    float kv[32];
+#pragma unroll
+    for (int d = 0; d < 32; ++d) kv[d] = ks[d0 + d];
+#pragma unroll
+    for (int d = 0; d < 32; ++d) s = s + qs[d0 + d] * kv[d];
+  }
+  return ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)i);
+}
+
+// Write the kept entries of a pair's list, in list order, given each
+// entry's keep flag: thread t handles entries [c0, c1), an exclusive prefix
+// sum of the per-thread counts (inclusive scan inside each wave, then the
+// totals of the waves before) gives its output position.
+template <typename Keep>
+__device__ __forceinline__ void compact_list(const SelParams& p, int u, int h, int e0, int n,
+                                             Keep keep, int* wave_tot) {
+  const int tid = (int)threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
+  int c = 0;
+  for (int i = c0; i < c1; ++i) c += keep(i);
+  const int lane = tid & 63;
+  int incl = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wave_tot[tid >> 6] = incl;
+  __syncthreads();
+  int before = incl - c;
+  for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
+  int32_t* out = p.lists + (int64_t)h * p.sp_total + p.sp_ptr[u] + before;
+  for (int i = c0; i < c1; ++i)
+    if (keep(i)) *out++ = p.pair_idx[e0 + i];
+}
+
+// A list longer than SELECT_SORT_ENTRIES: keys go to the workspace, and the
+// k-th largest key is found by a radix select, 8 bits per pass from the top
+// (a histogram of the next digit over the keys that match the digits chosen
+// so far; keys are unique, so after 8 passes the prefix is that key); then
+// the video entries with a key at or above it are kept.  Every loop is
+// bounded by n or by the 8 passes.
+__device__ void select_long_list(const SelParams& p, const float* qs, int u, int h, int e0, int n,
+                                 int* wave_tot) {
+  __shared__ unsigned hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_remain;
+  const int tid = (int)threadIdx.x;
+  uint64_t* kb = p.keys + (int64_t)h * p.pair_total + e0;
+  for (int i = tid; i < n; i += 256) kb[i] = entry_key(p, qs, h, e0, i);
+  __syncthreads();  // the workgroup's global writes are visible to it after the barrier
+  const int k = p.sp_keep[u];
+  uint64_t prefix = 0, mask = 0;
+  int remain = k;
+  for (int shift = 56; k > 0 && shift >= 0; shift -= 8) {
+    hist[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t key = kb[i];
+      if (key != 0 && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, b = 255;
+      for (; b > 0; --b) {
+        if (cum + (int)hist[b] >= remain) break;
+        cum += (int)hist[b];
+      }
+      s_prefix = prefix | ((uint64_t)b << shift);
+      s_remain = remain - cum;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    remain = s_remain;
+    mask |= (uint64_t)0xFF << shift;
+  }
+  const uint64_t threshold = prefix;
+  compact_list(p, u, h, e0, n,
+               [&](int i) {
+                 const uint64_t key = kb[i];
+                 return key == 0 || (k > 0 && key >= threshold);
+               },
+               wave_tot);
+}
+
 __global__ __launch_bounds__(256) void select_lists_kernel(SelParams p) {
   const int u = (int)blockIdx.x, h = (int)blockIdx.y, tid = (int)threadIdx.x;
   __shared__ float qs[128];
-  __shared__ uint64_t keys[SELECT_MAX_ENTRIES];
-  __shared__ uint8_t keep[SELECT_MAX_ENTRIES];
+  __shared__ uint64_t keys[SELECT_SORT_ENTRIES];
+  __shared__ uint8_t keep[SELECT_SORT_ENTRIES];
   __shared__ int wave_tot[4];
   const int e0 = p.pair_ptr[u], n = p.pair_ptr[u + 1] - e0;
   if (tid < 128) qs[tid] = p.q_sum[((int64_t)h * p.n_pairs + u) * 128 + tid];
+  __syncthreads();
+  if (n > SELECT_SORT_ENTRIES) {  // uniform: the whole workgroup
+    select_long_list(p, qs, u, h, e0, n, wave_tot);
+    return;
+  }
   int npow = 1;
   while (npow < n) npow <<= 1;
-  __syncthreads();
   // sort keys: (score order << 32) | ~index, descending = best score first,
   // lower index first among equal scores; entries that are not video tiles
   // (and the padding up to a power of two) get 0 and sort last
   for (int i = tid; i < npow; i += 256) {
-    uint64_t key = 0;
-    uint8_t kp = 0;
-    if (i < n) {
-      const int kt = p.pair_idx[e0 + i] >> 4;
-      if (p.video_tile[kt]) {
-        const float* ks = p.k_sum + ((int64_t)h * p.nkt + kt) * 128;
-        float s = 0.f;
-        // product and sum rounded separately (this file is built without
-        // floating-point contraction), ascending d; loads in batches of 32
-        for (int d0 = 0; d0 < 128; d0 += 32) {
-          float kv[32];
-#pragma unroll
-          for (int d = 0; d < 32; ++d) kv[d] = ks[d0 + d];
-#pragma unroll
-          for (int d = 0; d < 32; ++d) s = s + qs[d0 + d] * kv[d];
-        }
-        key = ((uint64_t)order_key(s) << 32) | (uint64_t)(~(uint32_t)i);
-      } else {
-        kp = 1;  // always kept
-      }
-    }
+    const uint64_t key = i < n ? entry_key(p, qs, h, e0, i) : 0;
     keys[i] = key;
-    keep[i] = kp;
+    keep[i] = i < n && key == 0;  // not a video tile: always kept
   }
   __syncthreads();
   for (int size = 2; size <= npow; size <<= 1) {
@@ -162,27 +248,7 @@ __global__ __launch_bounds__(256) void select_lists_kernel(SelParams p) {
   const int k = p.sp_keep[u];
   for (int r = tid; r < k; r += 256) keep[~(uint32_t)(keys[r] & 0xffffffffu)] = 1;
   __syncthreads();
-  // compaction in list order: thread t handles entries [c0, c1)
-  const int per = (n + 255) / 256;
-  const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
-  int c = 0;
-  for (int i = c0; i < c1; ++i) c += keep[i];
-  // exclusive prefix sum of c over the 256 threads: inclusive scan inside
-  // each wave, then the totals of the waves before this one
-  const int lane = tid & 63;
-  int incl = c;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
-  }
-  if (lane == 63) wave_tot[tid >> 6] = incl;
-  __syncthreads();
-  int before = incl - c;
-  for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
-  int32_t* out = p.lists + (int64_t)h * p.sp_total + p.sp_ptr[u] + before;
-  for (int i = c0; i < c1; ++i)
-    if (keep[i]) *out++ = p.pair_idx[e0 + i];
+  compact_list(p, u, h, e0, n, [&](int i) { return (int)keep[i]; }, wave_tot);
 }
 
 }  // namespace

@@ -379,3 +379,15 @@ def test_kvcache_adopt_records_existing_rows():
     nm.nomas_kvcache_reset(cache)
     assert lib.nomas_kvcache_adopt(c, arr, 1) == _lib.OK
     assert lib.nomas_kvcache_adopt(None, arr, 1) == _lib.ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.slow
+def test_plan_classes_training_pack_full_map():
+    """The whole 1,024 x 2,048 tile-class map of the 131072-token pack, bit
+    for bit against the oracle's (slow: every q-tile's mask is materialised)."""
+    w = wl.training_pack_131k()
+    t = oracle.expand(w.q_layout)
+    p = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=16, host_only=True)
+    cls = nm.nomas_plan_export_classes(p)
+    assert cls.shape == (1024, 2048)
+    np.testing.assert_array_equal(cls, oracle.tile_classes(t, t, 128, 64))

@@ -249,3 +249,46 @@ def test_sparse_lists_720p_long_session():
     say(f"720p session, 25% of video tiles: {total} entries per head")
     tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
     Selection(q, k, tq, tk, 25).check(lists, total)
+
+
+@pytest.mark.timeout(900)
+def test_sparse_lists_long_session_past_the_lds_sort():
+    """A 720p session of 40 cached segments (291,392 keys: about 4,550 key
+    tiles per query unit, past the 4,096 entries the in-LDS sort ranks): the
+    radix-select path, all heads, against the exact selection; and the
+    attention over its lists on sampled rows of units whose selection is
+    unambiguous."""
+    need_gpu()
+    w = wl.long_session_720p(n_cached=40)
+    kc, vc = w.cache_kv()
+    cache = new_cache(16, w.n_cached + w.n_new)
+    fill_cache(cache, w.cached, dev(kc), dev(vc))
+    rows = stored_rows(w.cached)
+    keys = as_stored(w.cached) + w.new
+    q, kn, vn = w.q(3), w.k_new(3), w.v_new(3)
+    plan = nm.nomas_attn_plan(w.q_layout, w.new, cache, heads=16, video_keep_percent=25)
+    o, lse, ws = run(plan, cache, dev(q), dev(kn), dev(vn))
+    lists, total = device_lists(plan, ws)
+    k = np.concatenate([kc[rows], kn])
+    del kc
+    tq, tk = oracle.expand(w.q_layout), oracle.expand(keys)
+    say(f"720p session, 40 cached segments: {len(tk)} keys, {total} entries per head")
+    assert (len(tk) + 63) // 64 > 4096
+    sel = Selection(q, k, tq, tk, 25)
+    ambiguous = sel.check(lists, total)
+    v = np.concatenate([vc[rows], vn])
+    del vc
+    # the ~4,550-tile lists have scores so close together that few units'
+    # selections are separated from the rest by the fp32 bound: the attention
+    # is compared on those units (every head that has one)
+    clear = sorted((h, u) for h in range(16) for u in range(sel.exact.shape[1])
+                   if (h, u) not in ambiguous)
+    say(f"  units with an unambiguous selection: {clear}")
+    assert clear
+    g = np.random.default_rng(17)
+    for h, u in clear[:4]:
+        rows_q = np.sort(g.choice(np.arange(u * UNIT, min(w.n_q, (u + 1) * UNIT)), 16, replace=False))
+        o_ref, l_ref, l_bnd = oracle_forward(q, k, v, tq, tk, SCALE, rows=rows_q, heads=[h],
+                                             tile_keep=sel.exact, unit_rows=UNIT, tile_keys=TILE)
+        check_o(host(o)[rows_q][:, [h]], o_ref, f"long sparse session, head {h} unit {u}")
+        check_lse(host(lse)[[h]][:, rows_q], l_ref, f"long sparse session, head {h} unit {u}", l_bnd)

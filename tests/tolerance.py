@@ -125,6 +125,23 @@ def lse_bound(q, k, tq, tk, scale, mode="R", rows=None, heads=None, window=0, bl
     return out
 
 
+def softmax_abs_v(q, k, v, tq, tk, scale, mode="R", rows=None, heads=None, block=512):
+    """sum_k P_qk |V_kd| per (row, head, dim) with P the exact softmax rows:
+    what a relative perturbation of P (at most r per element) can move O by
+    is at most r times this."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    heads = list(range(q.shape[1])) if heads is None else list(heads)
+    out = np.zeros((len(rows), len(heads), v.shape[2]))
+    for r0 in range(0, len(rows), block):
+        ridx = rows[r0:r0 + block]
+        m = oracle.visible_mask(tq.take(ridx), tk, mode)
+        for hi, h in enumerate(heads):
+            p, _, _ = _softmax_rows(q[ridx, h], k[:, h], m, scale)
+            out[r0:r0 + len(ridx), hi] = p @ np.abs(v[:, h])
+    return out
+
+
 def grad_sigma(q, k, v, d_o, tq, tk, scale, mode="R", heads=None, q_rows=None, k_rows=None,
                window=0, block=512):
     """Model standard deviations of the device dQ [len(q_rows), Hs, D] and
@@ -191,8 +208,8 @@ def score_bound(q, k, unit_rows, tile_keys):
     from oracle import sparse
     qs = sparse.block_sums(q, unit_rows)                  # [U, H, D]
     ks = sparse.block_sums(k, tile_keys)                  # [T, H, D]
-    qa = sparse.block_sums(np.abs(_f64(q)), unit_rows)
-    ka = sparse.block_sums(np.abs(_f64(k)), tile_keys)
+    qa = sparse.block_sums(np.abs(q), unit_rows)
+    ka = sparse.block_sums(np.abs(k), tile_keys)
     eq = gamma(unit_rows + 1) * qa
     ek = gamma(tile_keys + 1) * ka
     aq, ak = np.abs(qs), np.abs(ks)
