@@ -21,7 +21,8 @@ segments + the new one (120,896 keys read: the cache keeps video and head
 rows), then the append.
 training_pack (extra, not the headline) = forward and backward times on the
 131072-token training pack; backward effective TFLOP/s counts 8 D H A flops
-(four products) and, beside it, the FlashAttention convention 10 D H A.
+(four products) and, beside it, the FlashAttention convention 10 D H A;
+training_pack_kv_head_major: the same with K, V, dK, dV head-major.
 sparse_step (extra) = the 480p step with its last two denoising calls keeping
 25% of the video key tiles (video-block sparsity) and the first two dense.
 long_session_window4 (extra) = the same session with a sliding window of 4
@@ -208,15 +209,16 @@ def mfma_probe(torch, iters=20000):
             "frac_of_published_peak": round(tf.value / PEAK_BF16_TFLOPS, 4)}
 
 
-def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
+def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None, kv_head_major=False):
     """Forward + backward on the 131072-token training pack (4 videos, 16 heads,
     or `heads` of them: one GPU's share when heads are sharded): mean time of
     each over `iters` calls after `warmup`, HIP events on the launch stream.
+    kv_head_major: K, V, dK, dV in head-major [H][tokens][128] buffers.
     Inputs are drawn on the device (timing only)."""
     w = wl.training_pack_131k()
     H, D = heads or w.heads, 128
     t0 = time.perf_counter()
-    plan = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=H)
+    plan = nm.nomas_attn_plan(w.q_layout, w.q_layout, heads=H, kv_head_major=kv_head_major)
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info()
     A = info.unmasked_pairs
@@ -224,6 +226,8 @@ def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
     g.manual_seed(5000)
     mk = lambda: torch.randn((w.n_q, H, D), generator=g, device="cuda").to(torch.bfloat16)
     q, k, v, d_o = mk(), mk(), mk(), mk()
+    if kv_head_major:
+        k, v = k.permute(1, 0, 2).contiguous(), v.permute(1, 0, 2).contiguous()
     o = torch.empty_like(q)
     lse = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -244,6 +248,7 @@ def bench_training(nm, wl, torch, iters=5, warmup=2, heads=None):
             bwd_ms.append(e[1].elapsed_time(e[2]))
     f, b = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
     return {"workload": w.name, "tokens": w.n_q, "heads": H, "unmasked_pairs": A,
+            "kv_layout": "head-major" if kv_head_major else "token-major",
             "plan_host_ms": round(plan_ms, 2),
             "fwd_ms": round(f, 3), "fwd_tflops": round(4.0 * D * H * A / (f * 1e-3) / 1e12, 2),
             "bwd_ms": round(b, 3),
@@ -649,6 +654,7 @@ def main():
         line["long_session_window4"] = bench_long_session(nm, wl, torch, window=4)
     if not args.no_training:
         line["training_pack"] = bench_training(nm, wl, torch)
+        line["training_pack_kv_head_major"] = bench_training(nm, wl, torch, kv_head_major=True)
     if not args.no_sp8_share:
         # one GPU's share when the 16 heads are sharded over 8 GPUs (2 heads at
         # full sequence length): 58 query-tile units on 256 CUs, so every unit

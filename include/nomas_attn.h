@@ -112,9 +112,20 @@ enum { NOMAS_TEXT_QUERY_R = 0, NOMAS_TEXT_QUERY_K = 1, NOMAS_TEXT_QUERY_H = 2 };
 enum {
   NOMAS_PLAN_HOST_ONLY = 1, /* build host tables only (no device upload);
                                such a plan cannot run nomas_attn_fwd/bwd */
-  NOMAS_PLAN_GRAD_F32 = 2   /* nomas_attn_bwd writes dq, dk, dv as fp32
+  NOMAS_PLAN_GRAD_F32 = 2,  /* nomas_attn_bwd writes dq, dk, dv as fp32
                                (same layouts and element strides as the
                                bf16 gradients); without it they are bf16 */
+  NOMAS_PLAN_KV_HEAD_MAJOR = 4 /* the new-token keys and values are head-major:
+                               k_new / v_new of nomas_attn_fwd and k, v, dk,
+                               dv of nomas_attn_bwd are [H][n][128], row r of
+                               head h at element h * kv_stride + r * 128, and
+                               kv_stride (>= n * 128, a multiple of 8) is the
+                               stride between heads.  Without it they are
+                               token-major [n][H][128] with token stride
+                               kv_stride.  Queries, outputs and dO are
+                               token-major either way.  Head-major rows make
+                               each 64-key tile one contiguous 16 KB block
+                               per head, which streams faster from HBM. */
 };
 
 typedef struct {

@@ -23,6 +23,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_STALE_P
 TEXT_QUERY = {"R": 0, "K": 1, "H": 2}
 PLAN_HOST_ONLY = 1
 PLAN_GRAD_F32 = 2
+PLAN_KV_HEAD_MAJOR = 4
 TILE_EMPTY, TILE_FULL, TILE_PARTIAL = 0, 1, 2
 
 
@@ -189,15 +190,34 @@ def _token_stride(t, name, heads):
     return t.stride(0)
 
 
+def _head_stride(t, name, heads):
+    """Head stride of a head-major [heads, rows, 128] tensor with contiguous rows."""
+    if t is None:
+        return 0
+    if t.dim() != 3 or t.shape[0] != heads or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [{heads}, rows, {HEAD_DIM}] (head-major plan), got {tuple(t.shape)}")
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != HEAD_DIM):
+        raise ValueError(f"{name} must have contiguous rows of {HEAD_DIM}")
+    return t.stride(0)
+
+
+def _kv_stride(plan, t, name):
+    """The kv_stride argument for new-token K / V (or dK / dV) of this plan."""
+    if plan.kv_head_major:
+        return _head_stride(t, name, plan.heads)
+    return _token_stride(t, name, plan.heads)
+
+
 # ----------------------------------------------------------------------------
 # objects
 # ----------------------------------------------------------------------------
 
 class Plan:
-    def __init__(self, handle, heads, grad_f32=False):
+    def __init__(self, handle, heads, grad_f32=False, kv_head_major=False):
         self.handle = C.c_void_p(handle)
         self.heads = heads
         self.grad_f32 = grad_f32
+        self.kv_head_major = kv_head_major
 
     def info(self) -> nomas_plan_info:
         return nomas_plan_get_info(self)
@@ -256,17 +276,19 @@ class KVCache:
 # ----------------------------------------------------------------------------
 
 def nomas_attn_plan(q_layout, kv_layout, cache=None, *, heads=16, mode="R", host_only=False,
-                    block_q=0, block_k=0, window=0, video_keep_percent=0, grad_f32=False) -> Plan:
+                    block_q=0, block_k=0, window=0, video_keep_percent=0, grad_f32=False,
+                    kv_head_major=False) -> Plan:
     lib = load()
     ql, kl = _Layout(q_layout), _Layout(kv_layout)
-    flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_GRAD_F32 if grad_f32 else 0)
+    flags = ((PLAN_HOST_ONLY if host_only else 0) | (PLAN_GRAD_F32 if grad_f32 else 0) |
+             (PLAN_KV_HEAD_MAJOR if kv_head_major else 0))
     opts = nomas_plan_opts(heads, HEAD_DIM, block_q, block_k, TEXT_QUERY[mode], flags, window,
                            video_keep_percent)
     out = C.c_void_p()
     _check(lib.nomas_attn_plan(C.byref(ql.c), C.byref(kl.c),
                                cache.handle if cache is not None else None,
                                C.byref(opts), C.byref(out)), "nomas_attn_plan")
-    return Plan(out.value, heads, grad_f32)
+    return Plan(out.value, heads, grad_f32, kv_head_major)
 
 
 def nomas_plan_get_info(plan) -> nomas_plan_info:
@@ -295,10 +317,10 @@ def nomas_attn_fwd(plan, cache, q, k_new, v_new, o, lse=None, scale=HEAD_DIM ** 
     h = plan.heads
     qs = _token_stride(q, "q", h)
     os_ = _token_stride(o, "o", h)
-    ks = _token_stride(k_new, "k_new", h)
-    vs = _token_stride(v_new, "v_new", h)
+    ks = _kv_stride(plan, k_new, "k_new")
+    vs = _kv_stride(plan, v_new, "v_new")
     if k_new is not None and v_new is not None and ks != vs:
-        raise ValueError("k_new and v_new must share a token stride")
+        raise ValueError("k_new and v_new must share a stride")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().nomas_attn_fwd(plan.handle, cache.handle if cache is not None else None,
                                  _ptr(q), qs, _ptr(k_new), _ptr(v_new), ks, _ptr(o), os_,
@@ -311,10 +333,10 @@ def nomas_attn_fwd_noalloc(plan, cache, q, k_new, v_new, o, lse=None, scale=HEAD
     h = plan.heads
     qs = _token_stride(q, "q", h)
     os_ = _token_stride(o, "o", h)
-    ks = _token_stride(k_new, "k_new", h)
-    vs = _token_stride(v_new, "v_new", h)
+    ks = _kv_stride(plan, k_new, "k_new")
+    vs = _kv_stride(plan, v_new, "v_new")
     if k_new is not None and v_new is not None and ks != vs:
-        raise ValueError("k_new and v_new must share a token stride")
+        raise ValueError("k_new and v_new must share a stride")
     _check(load().nomas_attn_fwd_noalloc(plan.handle, cache.handle if cache is not None else None,
                                          _ptr(q), qs, _ptr(k_new), _ptr(v_new), ks, _ptr(o), os_,
                                          _ptr(lse), float(scale), _stream_ptr(stream, q)),
@@ -334,10 +356,10 @@ def nomas_attn_bwd(plan, q, k, v, o, d_o, lse, dq, dk, dv, scale=HEAD_DIM ** -0.
     for name, t in (("o", o), ("d_o", d_o), ("dq", dq)):
         if _token_stride(t, name, h) != qs:
             raise ValueError(f"{name} must share q's token stride")
-    ks = _token_stride(k, "k", h)
+    ks = _kv_stride(plan, k, "k")
     for name, t in (("v", v), ("dk", dk), ("dv", dv)):
-        if _token_stride(t, name, h) != ks:
-            raise ValueError(f"{name} must share k's token stride")
+        if _kv_stride(plan, t, name) != ks:
+            raise ValueError(f"{name} must share k's stride")
     want = "torch.float32" if plan.grad_f32 else "torch.bfloat16"
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is not None and str(t.dtype) != want:

@@ -145,6 +145,26 @@ nomas_status check_stride(int64_t stride, int32_t heads, const char* name) {
   return NOMAS_OK;
 }
 
+// Row and head strides of the new-token K / V (and dK / dV) rows from the
+// caller's kv_stride: token-major [n][H][128] (kv_stride = the token stride)
+// or, for plans built with NOMAS_PLAN_KV_HEAD_MAJOR, head-major [H][n][128]
+// (kv_stride = the head stride, at least n rows).
+nomas_status kv_strides(const nomas::HostPlan& h, int64_t kv_stride, int64_t n_rows, int64_t* row,
+                        int64_t* head) {
+  if (!h.kv_head_major) {
+    nomas_status s = check_stride(kv_stride, h.heads, "kv");
+    *row = kv_stride;
+    *head = NOMAS_HEAD_DIM;
+    return s;
+  }
+  if (kv_stride < n_rows * NOMAS_HEAD_DIM)
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "kv head stride < rows * 128 (head-major keys)");
+  if (kv_stride % 8 != 0) return fail(NOMAS_ERR_ALIGNMENT, "kv head stride not a multiple of 8");
+  *row = NOMAS_HEAD_DIM;
+  *head = kv_stride;
+  return NOMAS_OK;
+}
+
 nomas_status check_dev_ptr(const void* p, bool needed, const char* name) {
   if (!needed) return NOMAS_OK;
   if (!p) return fail(NOMAS_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
@@ -445,7 +465,8 @@ nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const voi
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NOMAS_ERR_ALIGNMENT, "lse misaligned");
   if ((s = check_stride(q_stride, h.heads, "q")) || (s = check_stride(o_stride, h.heads, "o")))
     return s;
-  if (has_new && (s = check_stride(kv_stride, h.heads, "kv"))) return s;
+  int64_t kv_row = NOMAS_HEAD_DIM, kv_head = NOMAS_HEAD_DIM;
+  if (has_new && (s = kv_strides(h, kv_stride, h.nk - h.n_cached, &kv_row, &kv_head))) return s;
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   const FwdWorkspace ws = fwd_workspace(h);
   size_t need = ws.total;
@@ -470,7 +491,8 @@ nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const voi
     sp.keys = ws.has_keys ? reinterpret_cast<uint64_t*>(wsb + ws.keys) : nullptr;
     sp.pair_total = h.pair_ptr.back();
     sp.q_stride = q_stride;
-    sp.kv_stride = kv_stride;
+    sp.kv_stride = kv_row;
+    sp.kv_head_stride = kv_head;
     sp.cache_cap = cache ? cache->capacity : 0;
     sp.sp_total = h.sp_total;
     sp.nq = (int32_t)h.nq;
@@ -511,7 +533,8 @@ nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const voi
   fp.groups = h.fwd_groups;
   fp.n_combine = (int32_t)h.combine.size();
   fp.q_stride = q_stride;
-  fp.kv_stride = kv_stride;
+  fp.kv_stride = kv_row;
+  fp.kv_head_stride = kv_head;
   fp.o_stride = o_stride;
   fp.cache_cap = cache ? cache->capacity : 0;
   fp.nq = (int32_t)h.nq;
@@ -589,7 +612,8 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
       (s = check_dev_ptr(dk, hk, "dk")) || (s = check_dev_ptr(dv, hk, "dv")) ||
       (s = check_dev_ptr(lse, hq, "lse")))
     return s;
-  if ((s = check_stride(q_stride, h.heads, "q")) || (s = check_stride(kv_stride, h.heads, "kv")))
+  int64_t kv_row = NOMAS_HEAD_DIM, kv_head = NOMAS_HEAD_DIM;
+  if ((s = check_stride(q_stride, h.heads, "q")) || (hk && (s = kv_strides(h, kv_stride, h.nk, &kv_row, &kv_head))))
     return s;
   size_t need = 0;
   nomas_attn_bwd_workspace_size(p, &need);
@@ -618,7 +642,8 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.kpair_ptr = p->d_kpair_ptr;
   bp.kpair_idx = p->d_kpair_idx;
   bp.q_stride = q_stride;
-  bp.kv_stride = kv_stride;
+  bp.kv_stride = kv_row;
+  bp.kv_head_stride = kv_head;
   bp.nq = (int32_t)h.nq;
   bp.nk = (int32_t)h.nk;
   bp.heads = h.heads;

@@ -187,11 +187,13 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int b = 2 * qh + bb;
-    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  Hidden pairs
-    // start their score chain at -inf and end there: P = 0 (uniform branch,
-    // so FULL tiles skip the selects).  Q and K enter unscaled and the fp32
-    // score is scaled once (the P of the dQ kernel, formed the same way).
-    // the dP chain starts from -delta of those queries and ends at dP - delta
+    // register i holds query 32 b + 16 (i / 8) + 8 hh + i % 8.  The score
+    // chain starts from zero (no register set-up: the first product takes a
+    // constant accumulator); hidden pairs get -inf after it, so P = 0
+    // (uniform branch: FULL tiles skip the selects).  Q and K enter unscaled
+    // and the fp32 score is scaled once (the P of the dQ kernel, formed the
+    // same way).  The dP chain starts from -delta of those queries and ends
+    // at dP - delta.
     f32x16 s = f32x16{}, dp;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -201,10 +203,6 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
       dp[4 * g + 1] = nd.y;
       dp[4 * g + 2] = nd.z;
       dp[4 * g + 3] = nd.w;
-    }
-    if (masked) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? 0.f : -INFINITY;
     }
     // the S / dP chains run at raised priority (as the forward's S^T block);
     // their A operands (Q, dO rows) are read one MFMA ahead, so that each
@@ -231,6 +229,10 @@ __device__ __forceinline__ void kv_qtile(KvWave& st, const char* stg, const int4
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product i
     }
     __builtin_amdgcn_s_setprio(0);
+    if (masked) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = ((vis >> (16 * bb + i)) & 1u) ? s[i] : -INFINITY;
+    }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -312,8 +314,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   KvWave st;
   {
     const int kr = key < p.nk ? key : p.nk - 1;  // rows past nk: computed, never stored
-    const uint16_t* ks = p.k + (int64_t)kr * p.kv_stride + (int64_t)h * D + 8 * hh;
-    const uint16_t* vs = p.v + (int64_t)kr * p.kv_stride + (int64_t)h * D + 8 * hh;
+    const int64_t row = (int64_t)kr * p.kv_stride + (int64_t)h * p.kv_head_stride + 8 * hh;
+    const uint16_t* ks = p.k + row;
+    const uint16_t* vs = p.v + row;
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
       st.kf[s8] = *reinterpret_cast<const bf16x8*>(ks + 16 * s8);
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
         st.dk[db][ri] += xk[(16 * db + ri) * 64];
       }
     if (key < p.nk) {
-      const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * D;
+      const int64_t off = (int64_t)key * p.kv_stride + (int64_t)h * p.kv_head_stride;
       if (p.grad_f32) {
         store_grad_row<true>(p.dv, off, st.dv, 1.f, hh);
         store_grad_row<true>(p.dk, off, st.dk, p.scale, hh);
@@ -558,10 +561,10 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
   lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
   lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
-  lc.k_cache_h = p.k + (int64_t)h * D;  // unused: no cached keys
-  lc.v_cache_h = p.v + (int64_t)h * D;
-  lc.k_new_h = p.k + (int64_t)h * D;
-  lc.v_new_h = p.v + (int64_t)h * D;
+  lc.k_cache_h = p.k;  // unused: no cached keys
+  lc.v_cache_h = p.v;
+  lc.k_new_h = p.k + (int64_t)h * p.kv_head_stride;
+  lc.v_new_h = p.v + (int64_t)h * p.kv_head_stride;
 
   const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
   const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];

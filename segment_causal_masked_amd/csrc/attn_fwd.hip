@@ -300,8 +300,8 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int n_ent = e_end - e_begin;
     lc.k_cache_h = p.k_cache + (int64_t)h * p.cache_cap * D;
     lc.v_cache_h = p.v_cache + (int64_t)h * p.cache_cap * D;
-    lc.k_new_h = p.k_new + (int64_t)h * D;
-    lc.v_new_h = p.v_new + (int64_t)h * D;
+    lc.k_new_h = p.k_new + (int64_t)h * p.kv_head_stride;
+    lc.v_new_h = p.v_new + (int64_t)h * p.kv_head_stride;
 
     if (qrow < p.nq) {
       const uint16_t* src = p.q + (int64_t)qrow * p.q_stride + (int64_t)h * D + 8 * hh;

@@ -20,7 +20,7 @@ struct FwdParams {
   const uint16_t* q;       // [nq][H][128] bf16, stride q_stride
   const uint16_t* k_cache; // [H][cap][128] bf16 (or null)
   const uint16_t* v_cache;
-  const uint16_t* k_new;   // [n_new][H][128] bf16, stride kv_stride
+  const uint16_t* k_new;   // new-token rows: row r of head h at r * kv_stride + h * kv_head_stride
   const uint16_t* v_new;
   uint16_t* o;             // [nq][H][128] bf16, stride o_stride
   float* lse;              // [H][nq] or null
@@ -35,7 +35,7 @@ struct FwdParams {
   int64_t list_head_stride;    // lists per head (sparse plans), else 0: unit (h, u')
                                // walks csr_idx + h * list_head_stride + csr_ptr[u']
   float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
-  int64_t q_stride, kv_stride, o_stride, cache_cap;
+  int64_t q_stride, kv_stride, kv_head_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;
   int32_t groups, n_combine, n_pairs;
   float scale_log2;        // softmax scale * log2(e)
@@ -54,7 +54,7 @@ hipError_t noalloc_scratch(int device, void** ptr);
 struct SelParams {
   const uint16_t* q;        // [nq][H][128] bf16, stride q_stride
   const uint16_t* k_cache;  // [H][cap][128] bf16 (or null)
-  const uint16_t* k_new;    // [n_new][H][128] bf16, stride kv_stride
+  const uint16_t* k_new;    // new-token rows, as in FwdParams
   const int32_t* pair_ptr;  // dense merged lists per pair (n_pairs + 1)
   const int32_t* pair_idx;  // (k_tile << 4) | flags
   const int32_t* sp_ptr;    // sparse list prefix per pair (n_pairs + 1)
@@ -65,7 +65,7 @@ struct SelParams {
   int32_t* lists;           // workspace [H][sp_total]
   uint64_t* keys;           // workspace [H][pair_total] (null unless some pair list
                             // is longer than SELECT_SORT_ENTRIES): sort keys of long lists
-  int64_t q_stride, kv_stride, cache_cap, sp_total, pair_total;
+  int64_t q_stride, kv_stride, kv_head_stride, cache_cap, sp_total, pair_total;
   int32_t nq, nk, n_cached, heads, nkt, n_pairs;
 };
 // Pair lists up to this length are ranked by a bitonic sort in LDS; longer
@@ -109,7 +109,7 @@ struct Int8ExpandParams {
 hipError_t launch_kvcache_int8_expand(const Int8ExpandParams& p, hipStream_t stream);
 
 struct BwdParams {
-  const uint16_t *q, *k, *v, *o, *d_o;  // [T][H][128] bf16 (q, o, d_o: q_stride; k, v: kv_stride)
+  const uint16_t *q, *k, *v, *o, *d_o;  // bf16; q, o, d_o: [T][H][128], token stride q_stride
   const float* lse;        // [H][nq], natural log (from the forward)
   uint16_t *dq, *dk, *dv;  // outputs, same layouts (element strides) as q / k / v;
                            // fp32 elements when grad_f32 != 0, else bf16
@@ -119,7 +119,8 @@ struct BwdParams {
   const KDescDev* kdesc;   // nkt*64 entries
   const int32_t *pair_ptr, *pair_idx;    // per q-tile pair: the forward's key-tile lists
   const int32_t *kpair_ptr, *kpair_idx;  // per key-tile pair: (q_tile << 4) | flags
-  int64_t q_stride, kv_stride;
+  int64_t q_stride, kv_stride, kv_head_stride;  // k, v, dk, dv: row r of head h at
+                                                // r * kv_stride + h * kv_head_stride
   int32_t nq, nk, heads, nqt, nkt, n_pairs, n_kpairs;
   int32_t grad_f32;
   float scale, scale_log2;

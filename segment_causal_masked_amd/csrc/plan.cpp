@@ -162,7 +162,7 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
     *err = "text_query_mode must be R (0), K (1) or H (2)";
     return NOMAS_ERR_INVALID_ARGUMENT;
   }
-  if (opts.flags & ~int32_t(NOMAS_PLAN_HOST_ONLY | NOMAS_PLAN_GRAD_F32)) { *err = "unknown plan flag"; return NOMAS_ERR_INVALID_ARGUMENT; }
+  if (opts.flags & ~int32_t(NOMAS_PLAN_HOST_ONLY | NOMAS_PLAN_GRAD_F32 | NOMAS_PLAN_KV_HEAD_MAJOR)) { *err = "unknown plan flag"; return NOMAS_ERR_INVALID_ARGUMENT; }
   if (opts.window_segments < 0) { *err = "window_segments must be >= 0"; return NOMAS_ERR_INVALID_ARGUMENT; }
   if (opts.video_keep_percent < 0 || opts.video_keep_percent > 100) {
     *err = "video_keep_percent must be in [0, 100]";
@@ -170,6 +170,7 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   }
   p.keep_percent = opts.video_keep_percent;
   p.grad_f32 = (opts.flags & NOMAS_PLAN_GRAD_F32) != 0;
+  p.kv_head_major = (opts.flags & NOMAS_PLAN_KV_HEAD_MAJOR) != 0;
   p.window = opts.window_segments;
   p.bq = opts.block_q ? opts.block_q : 128;
   p.bk = opts.block_k ? opts.block_k : 64;

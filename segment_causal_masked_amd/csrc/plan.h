@@ -82,6 +82,7 @@ struct HostPlan {
   // lists themselves are chosen on the device per head.
   int32_t keep_percent = 0, window = 0;
   bool grad_f32 = false;  // nomas_attn_bwd writes fp32 gradients (NOMAS_PLAN_GRAD_F32)
+  bool kv_head_major = false;  // new-token K / V (and dK / dV) are [H][n][128]
   std::vector<int32_t> video_tile;
   std::vector<int32_t> sp_ptr, sp_keep;
   int64_t sp_total = 0;

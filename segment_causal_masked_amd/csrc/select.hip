@@ -81,7 +81,7 @@ __global__ __launch_bounds__(128) void select_ksum_kernel(SelParams p) {
     const int key = kt * 64 + r;
     if (key >= p.nk) return nullptr;
     return (key < p.n_cached ? p.k_cache + ((int64_t)h * p.cache_cap + key) * 128
-                             : p.k_new + (int64_t)(key - p.n_cached) * p.kv_stride + (int64_t)h * 128) +
+                             : p.k_new + (int64_t)(key - p.n_cached) * p.kv_stride + (int64_t)h * p.kv_head_stride) +
            8 * dg;
   };
   block_row_sum<64>(row, p.k_sum + ((int64_t)h * p.nkt + kt) * 128, part);
