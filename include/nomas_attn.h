@@ -472,6 +472,25 @@ nomas_status nomas_camera_attn_fwd(const nomas_camera_plan* plan,
                                    float scale, void* hip_stream);
 
 /* --------------------------------------------------------------------------
+ * Action windows in latent frames
+ * ------------------------------------------------------------------------ */
+
+/* The latent frames an action acts on, from its span in pixel frames.  The
+ * video autoencoder compresses time 4x ("Summary (Overview)", Theoretical
+ * Foundation, Eq. 1: F pixel frames give floor((F - 1) / 4) + 1 latent
+ * frames); the grouping taken is the causal one that count implies: latent
+ * frame 0 holds pixel frame 0 alone, latent frame i >= 1 pixel frames
+ * 4i - 3 .. 4i, and frames of a trailing incomplete group belong to none.
+ * An action over pixel frames [first, end) of a segment of n_pixel_frames
+ * frames gets the window [*lo, *hi) of every latent frame holding one of
+ * its frames (the frame_lo / frame_hi of nomas_action); *lo == *hi when
+ * all of its frames are in the dropped trailing group.
+ * Errors: INVALID_ARGUMENT (NULL output, first < 0, end <= first,
+ * end > n_pixel_frames). */
+nomas_status nomas_action_latent_window(int64_t first, int64_t end, int64_t n_pixel_frames,
+                                        int32_t* lo, int32_t* hi);
+
+/* --------------------------------------------------------------------------
  * Errors
  * ------------------------------------------------------------------------ */
 

@@ -70,3 +70,28 @@ def expand(segments) -> TokenAttrs:
         return TokenAttrs(e, e, e.astype(np.int8), e, e, e, e)
     return TokenAttrs(*(np.concatenate(cols[k]) for k in
                         ("video", "seg", "kind", "frame", "act", "win_lo", "win_hi")))
+
+
+def latent_groups(n_pixel_frames: int) -> list:
+    """[Summary] Theoretical Foundation, Eq. 1: F pixel frames compress into
+    floor((F - 1) / 4) + 1 latent frames.  The grouping taken is the causal
+    one that count implies: the first latent frame is pixel frame 0 alone,
+    every later one the next four pixel frames; a trailing incomplete group
+    is dropped.  Returns the list of pixel-frame lists, one per latent frame."""
+    groups = [[0]] if n_pixel_frames >= 1 else []
+    t = 1
+    while t + 4 <= n_pixel_frames:
+        groups.append(list(range(t, t + 4)))
+        t += 4
+    return groups
+
+
+def action_latent_window(first: int, end: int, n_pixel_frames: int):
+    """Latent window [lo, hi) of an action over pixel frames [first, end):
+    the latent frames holding any of its frames (lo == hi, at the number of
+    latent frames, when none does)."""
+    groups = latent_groups(n_pixel_frames)
+    hit = [i for i, g in enumerate(groups) if any(first <= t < end for t in g)]
+    if not hit:
+        return len(groups), len(groups)
+    return min(hit), max(hit) + 1

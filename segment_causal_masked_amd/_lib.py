@@ -94,6 +94,7 @@ def load():
         "nomas_attn_fwd": [P, P, P, I64, P, P, I64, P, I64, P, F32, P, SZ, P],
         "nomas_attn_fwd_noalloc": [P, P, P, I64, P, P, I64, P, I64, P, F32, P],
         "nomas_attn_bwd_workspace_size": [P, C.POINTER(SZ)],
+        "nomas_action_latent_window": [I64, I64, I64, C.POINTER(I32), C.POINTER(I32)],
         "nomas_attn_bwd": [P, P, P, P, P, P, P, I64, I64, P, P, P, F32, P, SZ, P],
         "nomas_kvcache_create": [I32, I32, I64, P, P, C.POINTER(P)],
         "nomas_kvcache_append": [P, C.POINTER(nomas_segment), P, P, I64, P],
@@ -369,6 +370,15 @@ def nomas_attn_bwd(plan, q, k, v, o, d_o, lse, dq, dk, dv, scale=HEAD_DIM ** -0.
                                  _ptr(lse), qs, ks, _ptr(dq), _ptr(dk), _ptr(dv), float(scale),
                                  _ptr(workspace), ws_bytes, _stream_ptr(stream, q)),
            "nomas_attn_bwd")
+
+
+def nomas_action_latent_window(first, end, n_pixel_frames):
+    """(frame_lo, frame_hi) in latent frames of an action over pixel frames
+    [first, end) of a segment of n_pixel_frames frames."""
+    lo, hi = C.c_int32(), C.c_int32()
+    _check(load().nomas_action_latent_window(int(first), int(end), int(n_pixel_frames),
+                                             C.byref(lo), C.byref(hi)), "nomas_action_latent_window")
+    return lo.value, hi.value
 
 
 def nomas_kvcache_create(heads, capacity, k_buf, v_buf) -> KVCache:

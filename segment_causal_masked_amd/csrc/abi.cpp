@@ -184,6 +184,21 @@ nomas_status check_device(const nomas_plan* p) {
 
 extern "C" {
 
+nomas_status nomas_action_latent_window(int64_t first, int64_t end, int64_t n_pixel_frames,
+                                        int32_t* lo, int32_t* hi) {
+  if (!lo || !hi) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL output");
+  if (first < 0 || end <= first || end > n_pixel_frames)
+    return fail(NOMAS_ERR_INVALID_ARGUMENT, "need 0 <= first < end <= n_pixel_frames");
+  if (n_pixel_frames > (int64_t(1) << 33)) return fail(NOMAS_ERR_INVALID_ARGUMENT, "n_pixel_frames too large");
+  const int64_t n_latent = (n_pixel_frames - 1) / 4 + 1;  // Eq. 1
+  // pixel frame t sits in latent frame ceil(t / 4): 0 -> 0, 4i - 3 .. 4i -> i
+  const int64_t a = std::min((first + 3) / 4, n_latent);
+  const int64_t b = std::min((end - 1 + 3) / 4 + 1, n_latent);
+  *lo = int32_t(a);
+  *hi = int32_t(std::max(a, b));
+  return ok();
+}
+
 const char* nomas_status_string(nomas_status s) {
   switch (s) {
     case NOMAS_OK: return "ok";
