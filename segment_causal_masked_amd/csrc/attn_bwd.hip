@@ -611,6 +611,12 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   }
 
   if (qrow < p.nq) {
+    // a row that sees no key (padding) may have been computed unmasked on
+    // tiles no other row needs a mask for: its gradient is zero
+    if (st.qd.seg < 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
+    }
     const int64_t off = (int64_t)qrow * p.q_stride + (int64_t)h * D;
     if (p.grad_f32) store_grad_row<true>(p.dq, off, st.acc, p.scale, hh);
     else store_grad_row<false>(p.dq, off, st.acc, p.scale, hh);

@@ -210,7 +210,10 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const f32x16* acc,
                                           float m_run, float l_tot, int h, int qrow, int hh,
                                           bool write_lse) {
   if (qrow >= p.nq) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // a row with a zero sum sees no key: exact zeros, whatever its accumulator
+  // holds (a padding row may have been computed unmasked)
+  const bool dead = !(l_tot > 0.f);
+  const float inv = dead ? 0.f : 1.f / l_tot;
   uint16_t* dst = p.o + (int64_t)qrow * p.o_stride + (int64_t)h * D;
   for (int j = 0; j < ndb; ++j) {
     const int db = db0 + j;
@@ -220,6 +223,7 @@ __device__ __forceinline__ void store_row(const FwdParams& p, const f32x16* acc,
       uint2 pk;
       pk.x = (uint32_t)f2bf(acc[j][4 * g + 0] * inv) | ((uint32_t)f2bf(acc[j][4 * g + 1] * inv) << 16);
       pk.y = (uint32_t)f2bf(acc[j][4 * g + 2] * inv) | ((uint32_t)f2bf(acc[j][4 * g + 3] * inv) << 16);
+      if (dead) pk = uint2{0u, 0u};
       *reinterpret_cast<uint2*>(dst + d0) = pk;
     }
   }
@@ -366,20 +370,27 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
       if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, lb0, lk0, lb1, lk1);
     }
 
+    // Rows that see no key (padding) may have been computed unmasked on tiles
+    // that need no mask for any other row: a zero sum makes them O = 0,
+    // LSE = -inf, here and through the merge.
+    const float l_sum = ws.l_run + __shfl_xor(ws.l_run, 32);
+    const float l_tot = ws.qd.seg < 0 ? 0.f : l_sum;
     if (slot < 0) {
-      const float l_tot = ws.l_run + __shfl_xor(ws.l_run, 32);
       store_row(p, ws.acc, 0, 4, ws.m_run, l_tot, h, qrow, hh, true);
     } else {  // partial piece: O / l (bf16) and (m, l), thread-native layout
-      const float l_tot = ws.l_run + __shfl_xor(ws.l_run, 32);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      // (a zero sum: zeros and m = -inf, so the merge gives it no weight)
+      const bool dead = !(l_tot > 0.f);
+      const float inv = dead ? 0.f : 1.f / l_tot;
       uint32_t* dst = reinterpret_cast<uint32_t*>(p.partial) + (int64_t)slot * SLOT_WORDS + tid;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          dst[(8 * db + j) * NTHREADS] = (uint32_t)f2bf(ws.acc[db][2 * j] * inv) |
-                                         ((uint32_t)f2bf(ws.acc[db][2 * j + 1] * inv) << 16);
-      reinterpret_cast<float*>(dst)[32 * NTHREADS] = ws.m_run;
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t v = (uint32_t)f2bf(ws.acc[db][2 * j] * inv) |
+                             ((uint32_t)f2bf(ws.acc[db][2 * j + 1] * inv) << 16);
+          dst[(8 * db + j) * NTHREADS] = dead ? 0u : v;
+        }
+      reinterpret_cast<float*>(dst)[32 * NTHREADS] = dead ? -INFINITY : ws.m_run;
       reinterpret_cast<float*>(dst)[33 * NTHREADS] = l_tot;
     }
     wait_vm_all();  // stores retired before the next piece's load accounting

@@ -8,6 +8,8 @@
 // R / K / H as documented in nomas_attn.h.
 #include "plan.h"
 
+#include <cmath>
+
 #include <algorithm>
 #include <climits>
 #include <map>
@@ -306,14 +308,16 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
   for (int64_t i = 0; i < p.nqt; ++i) {
     const int64_t rows = std::min(p.nq, (i + 1) * p.bq) - i * p.bq;
     for (int64_t j = 0; j < p.nkt; ++j) {
-      bool any = false, all = true;
-      for (int32_t a = qt_runs[i].first; a <= qt_runs[i].second && (all || !any); ++a) {
+      bool any = false, all = true, live_all = true;
+      for (int32_t a = qt_runs[i].first; a <= qt_runs[i].second && (live_all || !any); ++a) {
         QDesc qd = qd_of(qr[a]);
+        const bool live = qd.seg >= 0;  // padding rows see no key
         for (int32_t b = kt_runs[j].first; b <= kt_runs[j].second; ++b) {
           bool v = visible(qd, kd_of(kr[b]));
           any |= v;
           all &= v;
-          if (any && !all) break;
+          live_all &= v || !live;
+          if (any && !live_all) break;
         }
       }
       uint8_t c = !any ? NOMAS_TILE_EMPTY : (all ? NOMAS_TILE_FULL : NOMAS_TILE_PARTIAL);
@@ -324,6 +328,7 @@ nomas_status build_host_plan(const std::vector<nomas_segment>& q,
       p.executed_pairs += rows * cols;
       const bool ragged_k = (j + 1) * p.bk > p.nk;
       p.csr_idx.push_back(int32_t((j << 1) | ((c == NOMAS_TILE_PARTIAL || ragged_k) ? 1 : 0)));
+      p.csr_live_mask.push_back(uint8_t((c == NOMAS_TILE_PARTIAL && !live_all) || ragged_k));
       col_count[size_t(j)]++;
     }
     p.csr_ptr[size_t(i + 1)] = int32_t(p.csr_idx.size());
@@ -356,9 +361,9 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
       const int32_t kb = ib < eb ? (p.csr_idx[size_t(ib)] >> 1) : INT32_MAX;
       const int32_t kt = std::min(ka, kb);
       int32_t flags = 0;
-      if (ka == kt) flags |= (p.csr_idx[size_t(ia++)] & 1);
+      if (ka == kt) flags |= p.csr_live_mask[size_t(ia++)];
       else flags |= 4;  // EMPTY for the first q-tile
-      if (kb == kt) flags |= (p.csr_idx[size_t(ib++)] & 1) << 1;
+      if (kb == kt) flags |= p.csr_live_mask[size_t(ib++)] << 1;
       else flags |= 8;  // EMPTY for the second q-tile (or it does not exist)
       p.pair_idx.push_back((kt << 4) | flags);
     }
@@ -394,61 +399,193 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   p.pieces.clear();
   p.combine.clear();
   p.n_slots = 0;
-  std::vector<std::vector<Piece>> per(static_cast<size_t>(groups));
-  auto bound = [&](int64_t g) { return (total * g) / groups; };
-  auto group_of = [&](int64_t it) {  // the range holding iteration `it`
-    int64_t g = (it * groups) / std::max<int64_t>(total, 1);
-    while (g + 1 < groups && bound(g + 1) <= it) ++g;
-    while (g > 0 && bound(g) > it) --g;
-    return std::min<int64_t>(g, groups - 1);
+  auto unit_len = [&](int64_t u) {
+    const int64_t pr = u % p.n_pairs;
+    return int64_t(lptr[size_t(pr + 1)] - lptr[size_t(pr)]);
   };
-  for (int64_t u = 0; u < n_units; ++u) {
-    const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
-    const int64_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
-    const int64_t start = h * row_total + lptr[size_t(pr)];
-    if (n == 0) {  // nothing visible: still owes zeros / -inf to its rows
-      per[size_t(group_of(std::min(start, std::max<int64_t>(total - 1, 0))))].push_back(
-          Piece{int32_t(u), 0, 0, -1});
-      continue;
-    }
-    const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
-    for (int64_t g = g0; g <= g1; ++g) {
-      const int64_t a = std::max(bound(g), start), b = std::min(bound(g + 1), start + n);
-      if (a >= b) continue;
-      per[size_t(g)].push_back(Piece{int32_t(u), int32_t(a - start), int32_t(b - start), -1});
-    }
-    int32_t made = 0;
-    for (int64_t g = g0; g <= g1; ++g)
-      if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u)) ++made;
-    if (made > 1) {
-      const int32_t first_slot = p.n_slots;
-      for (int64_t g = g0; g <= g1; ++g)
-        if (!per[size_t(g)].empty() && per[size_t(g)].back().unit == int32_t(u))
-          per[size_t(g)].back().slot = p.n_slots++;
-      p.combine.push_back(CombineItem{int32_t(u), first_slot, made, 0});
+  auto unit_start = [&](int64_t u) { return (u / p.n_pairs) * row_total + lptr[size_t(u % p.n_pairs)]; };
+
+  // Each workgroup takes a list of ranges of the (unit, entry) iterations, in
+  // unit order.  Plain schedule: `groups` equal contiguous ranges, one per
+  // workgroup; the workgroups of an XCD (consecutive ids: the kernel maps
+  // hardware workgroup b to b % 8 * (groups / 8) + b / 8) then hold
+  // consecutive ranges.  Phased schedule, for plans whose units fall into
+  // large groups with disjoint keys (the (head, video) groups of a training
+  // pack): the iterations are first cut into one equal share per XCD, each
+  // share into phases -- runs of units of one (head, video) -- and every
+  // phase into one equal range per workgroup of the XCD, so that at any time
+  // all workgroups of an XCD stream the same video's keys of one head (one
+  // working set per L2) instead of as many as they hold ranges.
+  const int32_t n_xcd = groups % 8 == 0 ? 8 : 1, per_xcd = groups / n_xcd;
+  std::vector<int64_t> group_key(size_t(n_units), 0);  // (head, video of the pair's first query)
+  {
+    int64_t key = -1;
+    for (int64_t u = 0; u < n_units; ++u) {
+      const int64_t pr = u % p.n_pairs;
+      int32_t video = -1;
+      for (int64_t r = 2 * pr * p.bq; r < std::min<int64_t>(2 * (pr + 1) * p.bq, p.nqt * p.bq); ++r)
+        if (p.qdesc[size_t(r)].seg >= 0) {
+          video = p.qdesc[size_t(r)].lo;
+          break;
+        }
+      // a pair of padding only joins the group before it
+      if (video >= 0 || key < 0 || key / (int64_t(1) << 31) != u / p.n_pairs)
+        key = (u / p.n_pairs) * (int64_t(1) << 31) + std::max(video, 0);
+      group_key[size_t(u)] = key;
     }
   }
-  // Rotation: the largest piece of each unit is aligned so that at time tau of
-  // its workgroup's range (tiles already done by that workgroup) it visits
-  // entry tau mod n.  The workgroups of an XCD (consecutive ranges, the same
-  // heads) then stream the same key tiles at about the same time and share
-  // them in that XCD's L2, instead of each walking its own offset.
+  bool phased = n_xcd > 1 && total > 0;
+  for (int64_t u = 0, run = 0; phased && u < n_units; ++u) {  // every group large enough
+    run = (u > 0 && group_key[size_t(u)] == group_key[size_t(u - 1)]) ? run + 1 : 1;
+    const bool last = u + 1 == n_units || group_key[size_t(u + 1)] != group_key[size_t(u)];
+    if (last && run < 2 * int64_t(per_xcd)) phased = false;
+  }
+  // Cuts are placed at equal estimated cost rather than equal iteration
+  // counts: a unit's entries cost 1 + MASKED_COST times the fraction of them
+  // that evaluate the per-element mask, and every unit a workgroup starts
+  // costs PIECE_COST more (its Q rows, pipeline fill and epilogue), both in
+  // units of one 64-key tile; measured on the training pack's forward, where
+  // equal iteration ranges left the workgroups holding many short units or
+  // the masked ones up to 30% behind the others.
+  constexpr double PIECE_COST = 4.0, MASKED_COST = 1.0;
+  // (A sparse list keeps every non-video tile, where the masked entries
+  // mostly are, so its masked count is estimated by the dense list's; at
+  // 100% kept the two plans get the same cuts.)
+  std::vector<double> w_unit(size_t(n_units), 1.0), c_start(size_t(n_units) + 1, 0.0);
+  {
+    std::vector<double> w_pair(size_t(p.n_pairs), 1.0);
+    for (int64_t pr = 0; pr < p.n_pairs; ++pr) {
+      const int32_t e0 = p.pair_ptr[size_t(pr)], e1 = p.pair_ptr[size_t(pr + 1)];
+      const int64_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
+      int64_t masked = 0;
+      for (int32_t e = e0; e < e1; ++e) masked += (p.pair_idx[size_t(e)] & 3) != 0;
+      if (n > 0) w_pair[size_t(pr)] = 1.0 + MASKED_COST * std::min(1.0, double(masked) / double(n));
+    }
+    for (int64_t u = 0; u < n_units; ++u) w_unit[size_t(u)] = w_pair[size_t(u % p.n_pairs)];
+  }
+  for (int64_t u = 0; u < n_units; ++u)
+    c_start[size_t(u + 1)] = c_start[size_t(u)] + (unit_len(u) ? PIECE_COST : 0.0) +
+                             double(unit_len(u)) * w_unit[size_t(u)];
+  // cost of the iterations before global iteration i, and the iteration at
+  // which a given cost is reached
+  auto cost_at = [&](int64_t i) {
+    int64_t lo = 0, hi = n_units - 1;  // last unit starting at or before i
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (unit_start(mid) <= i) lo = mid; else hi = mid - 1;
+    }
+    const int64_t j = std::max<int64_t>(0, std::min(i - unit_start(lo), unit_len(lo)));
+    return c_start[size_t(lo)] + (j > 0 ? PIECE_COST : 0.0) + double(j) * w_unit[size_t(lo)];
+  };
+  auto iter_at = [&](double c) -> int64_t {
+    if (c <= 0.0) return 0;
+    if (c >= c_start.back()) return total;
+    int64_t lo = 0, hi = n_units - 1;  // last unit whose start cost is <= c
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (c_start[size_t(mid)] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int64_t u = lo, n = unit_len(u);
+    const double in = c - c_start[size_t(u)] - (n ? PIECE_COST : 0.0);
+    const int64_t j = in <= 0.0 ? 0 : std::min<int64_t>(n, int64_t(std::llround(in / w_unit[size_t(u)])));
+    return unit_start(u) + j;
+  };
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> ranges(static_cast<size_t>(groups));
+  if (!phased) {
+    const double T = c_start.back();
+    for (int64_t g = 0; g < groups; ++g)
+      ranges[size_t(g)].push_back({iter_at(T * double(g) / groups), iter_at(T * double(g + 1) / groups)});
+  } else {
+    const double T = c_start.back();
+    int64_t u = 0;
+    for (int32_t x = 0; x < n_xcd; ++x) {
+      const int64_t s0 = iter_at(T * x / n_xcd), s1 = iter_at(T * (x + 1) / n_xcd);
+      int64_t a = s0;
+      while (a < s1) {
+        while (u < n_units && unit_start(u) + unit_len(u) <= a) ++u;
+        // the phase: from a to the end of u's group (or of the share)
+        int64_t v = u;
+        while (v + 1 < n_units && group_key[size_t(v + 1)] == group_key[size_t(u)]) ++v;
+        const int64_t b = std::min(s1, unit_start(v) + unit_len(v));
+        const double ca = cost_at(a), cb = cost_at(b);
+        int64_t prev = a;
+        for (int32_t i = 0; i < per_xcd; ++i) {
+          const int64_t next = i + 1 == per_xcd ? b : std::min(b, std::max(prev, iter_at(ca + (cb - ca) * (i + 1) / per_xcd)));
+          ranges[size_t(x * per_xcd + i)].push_back({prev, next});
+          prev = next;
+        }
+        a = b;
+      }
+    }
+  }
+
+  // pieces: the units each range overlaps; a workgroup's time tau counts the
+  // iterations it has done before a piece
+  std::vector<int64_t> ustart(size_t(n_units) + 1, 0);
+  for (int64_t u = 0; u < n_units; ++u) ustart[size_t(u)] = unit_start(u);
+  ustart[size_t(n_units)] = total;
+  std::vector<std::vector<Piece>> per(static_cast<size_t>(groups));
+  std::vector<std::vector<int64_t>> tau(static_cast<size_t>(groups));
+  std::vector<int32_t> n_pc(size_t(n_units), 0);
+  for (int64_t g = 0; g < groups; ++g) {
+    int64_t done = 0;
+    for (const auto& rg : ranges[size_t(g)]) {
+      if (rg.first >= rg.second) continue;
+      int64_t u = int64_t(std::upper_bound(ustart.begin(), ustart.end() - 1, rg.first) - ustart.begin()) - 1;
+      for (; u < n_units && ustart[size_t(u)] < rg.second; ++u) {
+        const int64_t n = unit_len(u), st = ustart[size_t(u)];
+        const int64_t a = std::max(rg.first, st), b = std::min(rg.second, st + n);
+        if (a >= b) continue;
+        per[size_t(g)].push_back(Piece{int32_t(u), int32_t(a - st), int32_t(b - st), -1});
+        tau[size_t(g)].push_back(done + (a - rg.first));
+        ++n_pc[size_t(u)];
+      }
+      done += rg.second - rg.first;
+    }
+  }
+  // units with nothing visible still owe zeros / -inf to their rows: the
+  // workgroup whose range holds their position (or the last) writes them
+  for (int64_t u = 0; u < n_units; ++u) {
+    if (unit_len(u) != 0) continue;
+    const int64_t pos = std::min(ustart[size_t(u)], std::max<int64_t>(total - 1, 0));
+    int64_t owner = groups - 1;
+    for (int64_t g = 0; g < groups && owner == groups - 1; ++g)
+      for (const auto& rg : ranges[size_t(g)])
+        if (rg.first <= pos && pos < rg.second) {
+          owner = g;
+          break;
+        }
+    per[size_t(owner)].push_back(Piece{int32_t(u), 0, 0, -1});
+    tau[size_t(owner)].push_back(0);
+    ++n_pc[size_t(u)];
+  }
+  // slots and merge items for split units (slots of a unit are consecutive)
+  std::vector<int32_t> first_slot(size_t(n_units), -1), next_slot(size_t(n_units), 0);
+  for (int64_t u = 0; u < n_units; ++u)
+    if (n_pc[size_t(u)] > 1) {
+      first_slot[size_t(u)] = p.n_slots;
+      p.combine.push_back(CombineItem{int32_t(u), p.n_slots, n_pc[size_t(u)], 0});
+      p.n_slots += n_pc[size_t(u)];
+    }
+  // Rotation: the largest piece of each unit is aligned so that at time tau
+  // of its workgroup it visits entry tau mod n.  Workgroups of an XCD that
+  // work on units of equal length then stream the same key tiles at about
+  // the same time and share them in that XCD's L2.
   p.unit_shift.assign(size_t(n_units), 0);
-  for (int64_t u = 0; u < n_units; ++u) {
-    const int64_t h = u / p.n_pairs, pr = u % p.n_pairs;
-    const int64_t n = lptr[size_t(pr + 1)] - lptr[size_t(pr)];
-    if (n == 0) continue;
-    const int64_t start = h * row_total + lptr[size_t(pr)];
-    const int64_t g0 = group_of(start), g1 = group_of(start + n - 1);
-    int64_t best_g = g0, best_len = -1;
-    for (int64_t g = g0; g <= g1; ++g) {
-      const int64_t a = std::max(bound(g), start), b = std::min(bound(g + 1), start + n);
-      if (b - a > best_len) best_len = b - a, best_g = g;
+  std::vector<int64_t> best_len(size_t(n_units), -1);
+  for (int64_t g = 0; g < groups; ++g)
+    for (size_t i = 0; i < per[size_t(g)].size(); ++i) {
+      Piece& pc = per[size_t(g)][i];
+      const int64_t u = pc.unit, n = unit_len(u);
+      if (first_slot[size_t(u)] >= 0) pc.slot = first_slot[size_t(u)] + next_slot[size_t(u)]++;
+      if (n == 0) continue;
+      if (pc.e_end - pc.e_begin > best_len[size_t(u)]) {
+        best_len[size_t(u)] = pc.e_end - pc.e_begin;
+        // local index j of this piece runs at time tau + (j - e_begin)
+        const int64_t shift = ((tau[size_t(g)][i] - pc.e_begin) % n + n) % n;
+        p.unit_shift[size_t(u)] = int32_t(shift);
+      }
     }
-    // at local index j the workgroup has done (start + j - bound(best_g)) tiles
-    const int64_t shift = (start - bound(best_g)) % n;
-    p.unit_shift[size_t(u)] = int32_t((shift + n) % n);
-  }
   p.wg_ptr.assign(size_t(groups) + 1, 0);
   for (int32_t g = 0; g < groups; ++g) {
     p.pieces.insert(p.pieces.end(), per[size_t(g)].begin(), per[size_t(g)].end());
@@ -550,8 +687,16 @@ std::string validate_host_plan(const HostPlan& p) {
         const int64_t qt = 2 * u + half;
         const bool empty = qt >= p.nqt || p.classes[size_t(qt * p.nkt + t)] == NOMAS_TILE_EMPTY;
         if (empty != bool((v >> (2 + half)) & 1)) return bad("pair EMPTY flag vs class map");
-        if (!empty && p.classes[size_t(qt * p.nkt + t)] == NOMAS_TILE_PARTIAL && !((v >> half) & 1))
-          return bad("pair mask flag vs class map");
+        if (!empty && p.classes[size_t(qt * p.nkt + t)] == NOMAS_TILE_PARTIAL && !((v >> half) & 1)) {
+          // allowed only if the tile's hidden pairs all belong to rows that
+          // see no key at all (computed unmasked, written as zeros)
+          for (int64_t r = qt * p.bq; r < std::min(p.nq, (qt + 1) * p.bq); ++r) {
+            const QDesc& qd = p.qdesc[size_t(r)];
+            if (qd.seg < 0) continue;
+            for (int64_t k = t * p.bk; k < (t + 1) * p.bk; ++k)
+              if (k >= p.nk || !visible(qd, p.kdesc[size_t(k)])) return bad("pair mask flag vs class map");
+          }
+        }
       }
       prev = t;
     }

@@ -62,6 +62,11 @@ struct HostPlan {
   std::vector<KDesc> kdesc;   // nkt * bk entries (tail padded with seg = -1)
   std::vector<uint8_t> classes;  // nqt * nkt, NOMAS_TILE_*
   std::vector<int32_t> csr_ptr, csr_idx;  // per q-tile
+  // per CSR entry: 1 if some query of the tile that sees any key at all (a
+  // live row: not padding) misses a key of the tile, or the key tile is
+  // ragged -- the per-element mask the forward and dQ kernels need.  Rows
+  // that see no key are computed unmasked there and written as zeros.
+  std::vector<uint8_t> csr_live_mask;
   std::vector<int32_t> csc_ptr, csc_idx;  // per k-tile
   int64_t n_empty = 0, n_full = 0, n_partial = 0;
   int64_t unmasked_pairs = 0, executed_pairs = 0;

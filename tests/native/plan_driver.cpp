@@ -71,7 +71,7 @@ int main() {
         continue;
       }
       nomas::build_fwd_schedule(&plan, 256);
-      std::vector<nomas::HostPlan> bad(6, plan);
+      std::vector<nomas::HostPlan> bad(7, plan);
       bad[0].pieces.pop_back();                          // a unit's tail left uncovered
       bad[0].wg_ptr.back() -= 1;
       std::swap(bad[1].csr_idx[0], bad[1].csr_idx[1]);   // list out of order
@@ -82,6 +82,17 @@ int main() {
       bad[3].pieces[0].e_end += 1;                       // a piece past its list
       bad[4].combine.clear();                            // split units never merged
       bad[5].unit_shift[0] = 1 << 30;                    // rotation out of range
+      // the mask bit of the first entry whose q-tile has a row that sees
+      // keys but misses one of this tile's, cleared
+      for (size_t e = 0, qt = 0; e < plan.csr_idx.size(); ++e) {
+        while (plan.csr_ptr[qt + 1] <= int32_t(e)) ++qt;
+        if (!plan.csr_live_mask[e] || plan.classes[qt * plan.nkt + (plan.csr_idx[e] >> 1)] != NOMAS_TILE_PARTIAL)
+          continue;
+        const int32_t kt = plan.csr_idx[e] >> 1, u = int32_t(qt / 2), bit = 1 << (qt % 2);
+        for (int32_t i = plan.pair_ptr[u]; i < plan.pair_ptr[u + 1]; ++i)
+          if ((plan.pair_idx[i] >> 4) == kt) bad[6].pair_idx[i] &= ~bit;
+        break;
+      }
       int caught = 0;
       for (const auto& b : bad) caught += !nomas::validate_host_plan(b).empty();
       std::printf("caught %d %zu\n", caught, bad.size());

@@ -110,9 +110,10 @@ def test_malformed_records_rejected_cleanly(driver):
 def test_invariant_check_catches_planted_mistakes(driver):
     """Copies of the 480p step's plan with one mistake each (an uncovered
     iteration, a list out of order, a list entry on an EMPTY tile, a piece
-    past its list, split units never merged, a rotation out of range): the
+    past its list, split units never merged, a rotation out of range, a mask
+    bit cleared on a tile where a row that sees keys misses one): the
     invariant check flags every one."""
     w = wl.cached_step_480p()
     c = case(w.q_layout, w.cached, w.new).replace("\nE", "\nX")
     out = run(driver, [c])
-    assert out == ["caught 6 6"], out
+    assert out == ["caught 7 7"], out
