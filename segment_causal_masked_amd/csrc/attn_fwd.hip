@@ -12,8 +12,8 @@
 // 128-query tiles of one head (256 queries, one per lane column of the eight
 // waves of a workgroup, two waves per SIMD); its key tiles are the union of the
 // pair's tile lists, with per-q-tile EMPTY / mask flags.  The host cuts the
-// (unit, key tile) iterations into equal contiguous ranges, one per workgroup
-// (one per CU).  Each K/V tile fetched serves 256 queries, and the 130 KB of
+// (unit, key tile) iterations into ranges of equal estimated cost, one per
+// workgroup (one per CU).  Each K/V tile fetched serves 256 queries, and the 130 KB of
 // LDS hold four tile stages used as two pairs: a pair of tiles is computed
 // while the next pair loads, with one barrier per pair.  A unit
 // split between ranges is

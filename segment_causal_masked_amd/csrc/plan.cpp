@@ -406,16 +406,17 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
   auto unit_start = [&](int64_t u) { return (u / p.n_pairs) * row_total + lptr[size_t(u % p.n_pairs)]; };
 
   // Each workgroup takes a list of ranges of the (unit, entry) iterations, in
-  // unit order.  Plain schedule: `groups` equal contiguous ranges, one per
-  // workgroup; the workgroups of an XCD (consecutive ids: the kernel maps
-  // hardware workgroup b to b % 8 * (groups / 8) + b / 8) then hold
-  // consecutive ranges.  Phased schedule, for plans whose units fall into
-  // large groups with disjoint keys (the (head, video) groups of a training
-  // pack): the iterations are first cut into one equal share per XCD, each
-  // share into phases -- runs of units of one (head, video) -- and every
-  // phase into one equal range per workgroup of the XCD, so that at any time
-  // all workgroups of an XCD stream the same video's keys of one head (one
-  // working set per L2) instead of as many as they hold ranges.
+  // unit order.  Plain schedule: `groups` contiguous ranges of equal cost
+  // (below), one per workgroup; the workgroups of an XCD (consecutive ids:
+  // the kernel maps hardware workgroup b to b % 8 * (groups / 8) + b / 8)
+  // then hold consecutive ranges.  Phased schedule, for plans whose units
+  // fall into large groups with disjoint keys (the (head, video) groups of a
+  // training pack): the iterations are first cut into one share of equal
+  // cost per XCD, each share into phases -- runs of units of one (head,
+  // video) -- and every phase into one range of equal cost per workgroup of
+  // the XCD, so that at any time all workgroups of an XCD stream the same
+  // video's keys of one head (one working set per L2) instead of as many as
+  // they hold ranges.
   const int32_t n_xcd = groups % 8 == 0 ? 8 : 1, per_xcd = groups / n_xcd;
   std::vector<int64_t> group_key(size_t(n_units), 0);  // (head, video of the pair's first query)
   {

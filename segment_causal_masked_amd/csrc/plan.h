@@ -42,8 +42,9 @@ inline bool visible(const QDesc& q, const KDesc& k) {
 // = (k_tile << 4) | flags: bit 0 / 1 = the first / second q-tile needs the
 // per-element mask there, bit 2 / 3 = the tile is EMPTY for the first /
 // second q-tile (its waves skip it).  The (unit, entry) iterations are cut
-// into `groups` contiguous, equal ranges, one per persistent workgroup; a unit
-// cut by a range boundary becomes several pieces whose partial results are
+// into ranges of equal estimated cost, one or (training packs, in phases of
+// one head and video per XCD) several per persistent workgroup; a unit cut
+// by a range boundary becomes several pieces whose partial results are
 // merged afterwards.
 struct Piece {
   int32_t unit, e_begin, e_end, slot;  // slot = partial-result slot, -1 = final
@@ -99,7 +100,8 @@ struct HostPlan {
   std::vector<int32_t> kpair_ptr, kpair_idx;
 };
 
-// Cut the forward iterations into `groups` equal contiguous ranges.
+// Cut the forward iterations into ranges of equal estimated cost for `groups`
+// persistent workgroups.
 void build_fwd_schedule(HostPlan* p, int32_t groups);
 
 // Merged per-key-tile-pair lists for the dK / dV kernel.
