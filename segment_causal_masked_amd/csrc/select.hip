@@ -21,7 +21,7 @@
 // from the exact one only between tiles whose exact scores are closer than
 // the rounding error of that evaluation.
 //
-// Three launches: key-tile sums, query-pair sums, then one workgroup per
+// Two launches: the key-tile and query-pair sums, then one workgroup per
 // (pair, head) that scores, ranks (a bitonic sort in LDS, or for lists of
 // more than 4096 entries a radix select over keys in the workspace) and
 // compacts the list.
@@ -72,31 +72,32 @@ __device__ __forceinline__ void block_row_sum(RowPtr row_ptr, float* out, float*
   }
 }
 
-// ksum of every video key tile: one workgroup per (tile, head).
-__global__ __launch_bounds__(128) void select_ksum_kernel(SelParams p) {
-  const int kt = (int)blockIdx.x, h = (int)blockIdx.y;
-  __shared__ float part[(64 / GROUP) * 128];
-  if (!p.video_tile[kt]) return;
-  auto row = [&](int r, int dg) -> const uint16_t* {
-    const int key = kt * 64 + r;
-    if (key >= p.nk) return nullptr;
-    return (key < p.n_cached ? p.k_cache + ((int64_t)h * p.cache_cap + key) * 128
-                             : p.k_new + (int64_t)(key - p.n_cached) * p.kv_stride + (int64_t)h * p.kv_head_stride) +
-           8 * dg;
-  };
-  block_row_sum<64>(row, p.k_sum + ((int64_t)h * p.nkt + kt) * 128, part);
-}
-
-// qsum of every query-tile pair: one workgroup per (pair, head).
-__global__ __launch_bounds__(256) void select_qsum_kernel(SelParams p) {
-  const int u = (int)blockIdx.x, h = (int)blockIdx.y;
+// One launch for both kinds of sums, one workgroup per (item, head): items
+// 0 .. nkt - 1 are key tiles (ksum of every video key tile), the rest
+// query-tile pairs (qsum).  The branch is uniform per workgroup.
+__global__ __launch_bounds__(256) void select_sums_kernel(SelParams p) {
+  const int item = (int)blockIdx.x, h = (int)blockIdx.y;
   __shared__ float part[(256 / GROUP) * 128];
-  auto row = [&](int r, int dg) -> const uint16_t* {
-    const int q = u * 256 + r;
-    if (q >= p.nq) return nullptr;
-    return p.q + (int64_t)q * p.q_stride + (int64_t)h * 128 + 8 * dg;
-  };
-  block_row_sum<256>(row, p.q_sum + ((int64_t)h * p.n_pairs + u) * 128, part);
+  if (item < p.nkt) {
+    const int kt = item;
+    if (!p.video_tile[kt]) return;
+    auto row = [&](int r, int dg) -> const uint16_t* {
+      const int key = kt * 64 + r;
+      if (key >= p.nk) return nullptr;
+      return (key < p.n_cached ? p.k_cache + ((int64_t)h * p.cache_cap + key) * 128
+                               : p.k_new + (int64_t)(key - p.n_cached) * p.kv_stride + (int64_t)h * p.kv_head_stride) +
+             8 * dg;
+    };
+    block_row_sum<64>(row, p.k_sum + ((int64_t)h * p.nkt + kt) * 128, part);
+  } else {
+    const int u = item - p.nkt;
+    auto row = [&](int r, int dg) -> const uint16_t* {
+      const int q = u * 256 + r;
+      if (q >= p.nq) return nullptr;
+      return p.q + (int64_t)q * p.q_stride + (int64_t)h * 128 + 8 * dg;
+    };
+    block_row_sum<256>(row, p.q_sum + ((int64_t)h * p.n_pairs + u) * 128, part);
+  }
 }
 
 // fp32 -> uint32 with the same order (negative values reversed)
@@ -254,14 +255,11 @@ __global__ __launch_bounds__(256) void select_lists_kernel(SelParams p) {
 }  // namespace
 
 hipError_t launch_select(const SelParams& p, hipStream_t stream) {
-  if (p.nkt > 0)
-    hipLaunchKernelGGL(select_ksum_kernel, dim3((unsigned)p.nkt, (unsigned)p.heads), dim3(128), 0,
-                       stream, p);
+  if (p.n_pairs == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_sums_kernel, dim3((unsigned)(p.nkt + p.n_pairs), (unsigned)p.heads),
+                     dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_pairs == 0) return e;
-  hipLaunchKernelGGL(select_qsum_kernel, dim3((unsigned)p.n_pairs, (unsigned)p.heads), dim3(256), 0,
-                     stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_lists_kernel, dim3((unsigned)p.n_pairs, (unsigned)p.heads), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
