@@ -199,6 +199,50 @@ def test_padding_rows_and_ragged_shapes():
     assert (host(o)[pad] == 0).all()
 
 
+def test_padding_rows_have_no_influence_bitwise():
+    """Rows that see no key (padding) are computed unmasked on tiles where
+    every other row of the tile sees every key, and written as exact zeros.
+    So whatever the padding rows of Q hold -- large values, NaN -- the live
+    rows' O and LSE stay bit-identical and the padding rows stay O = 0,
+    LSE = -inf; in the backward, finite garbage in the padding rows of Q and
+    dO changes no bit of dK, dV or the live rows of dQ, and their own dQ rows
+    are 0."""
+    need_gpu()
+    segs = [wl.Segment(0, 0, 4, 40, 8, [(6, 0, 2)], n_pad=70),
+            wl.Segment(0, 1, 4, 40, 8, [(5, 1, 3)], n_pad=90),
+            wl.Segment(1, 0, 5, 37, 6, [(4, 0, 5)], n_pad=45)]
+    n, heads = wl.layout_tokens(segs), 2
+    t = oracle.expand(segs)
+    pad = torch.from_numpy(t.kind == oracle.PAD).to("cuda")
+    say(f"padding rows: {n} tokens, {int(pad.sum())} of them padding, {heads} heads")
+    plan = nm.nomas_attn_plan(segs, segs, heads=heads)
+    q, k, v, d_o = (dev(wl.randn((n, heads, 128), 7400 + i)) for i in range(4))
+    o0, l0 = run_fwd(plan, None, q, k, v, heads)
+    assert (o0[pad] == 0).all() and torch.isinf(l0[:, pad]).all() and (l0[:, pad] < 0).all()
+    for what, fill in (("large", 3.0e4), ("NaN", float("nan"))):
+        qg = q.clone()
+        qg[pad] = fill
+        o1, l1 = run_fwd(plan, None, qg, k, v, heads)
+        assert torch.equal(o1.view(torch.int16), o0.view(torch.int16)), what
+        assert torch.equal(l1, l0), what
+    # backward: finite garbage in the padding rows of Q and dO
+    gd = torch.bfloat16
+    def bwd(qx, dox):
+        dq, dk, dv = (torch.empty((n, heads, 128), dtype=gd, device="cuda") for _ in range(3))
+        ws = torch.empty(max(nm.nomas_attn_bwd_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+        nm.nomas_attn_bwd(plan, qx, k, v, o0, dox, l0, dq, dk, dv, SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        return dq, dk, dv
+    base = bwd(q, d_o)
+    qg, dog = q.clone(), d_o.clone()
+    qg[pad] = 1.0e3
+    dog[pad] = -2.0e3
+    got = bwd(qg, dog)
+    for b, g2, name in zip(base, got, ("dQ", "dK", "dV")):
+        assert torch.equal(b.view(torch.int16), g2.view(torch.int16)), name
+    assert (got[0][pad] == 0).all()
+
+
 def test_thirty_two_actions_and_many_cached_segments():
     """The largest action count a segment may carry (32: every bit of the
     descriptors' tail masks in use) and a cache of 40 small segments, as a
