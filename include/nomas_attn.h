@@ -35,7 +35,8 @@
  *     be 16-byte aligned;
  *   - LSE is fp32 [heads][queries] (natural log; -inf for a row that sees no
  *     key); such rows (padding) get O = 0 and dQ = 0 whatever their inputs
- *     hold, and never change another row's result;
+ *     hold, and finite values in them change no other result (in the
+ *     forward not even non-finite ones);
  *   - device work is enqueued on the caller's HIP stream (NULL = default
  *     stream) and is not waited for;
  *   - plans and caches are library-owned handles; K/V cache storage, outputs
