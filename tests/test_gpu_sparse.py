@@ -292,3 +292,36 @@ def test_sparse_lists_long_session_past_the_lds_sort():
                                              tile_keep=sel.exact, unit_rows=UNIT, tile_keys=TILE)
         check_o(host(o)[rows_q][:, [h]], o_ref, f"long sparse session, head {h} unit {u}")
         check_lse(host(lse)[[h]][:, rows_q], l_ref, f"long sparse session, head {h} unit {u}", l_bnd)
+
+
+def test_sparse_training_pack_phased_schedule():
+    """A pack of two 16,384-token videos (64 query-tile pairs per (head,
+    video): its plans take the phased schedule, each XCD on one head's video
+    at a time).  Keeping every video tile equals the dense call bit for bit
+    (both plans get the same cuts); at 25% the lists are checked against the
+    exact selection and the attention against the oracle on sampled rows of
+    units whose selection is unambiguous."""
+    need_gpu()
+    segs = wl.pack_layout(wl.rng(8080), 2, 16384)
+    n = wl.layout_tokens(segs)
+    say(f"sparse training pack: {n} tokens, 2 videos, 16 heads")
+    q, k, v = (wl.randn((n, 16, 128), 8100 + i) for i in range(3))
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    o_d, l_d, _ = run(nm.nomas_attn_plan(segs, segs, heads=16), None, qd, kd, vd)
+    o_a, l_a, _ = run(nm.nomas_attn_plan(segs, segs, heads=16, video_keep_percent=100), None, qd, kd, vd)
+    assert torch.equal(o_a.view(torch.int16), o_d.view(torch.int16)) and torch.equal(l_a, l_d)
+    plan = nm.nomas_attn_plan(segs, segs, heads=16, video_keep_percent=25)
+    o, lse, ws = run(plan, None, qd, kd, vd)
+    lists, total = device_lists(plan, ws)
+    t = oracle.expand(segs)
+    sel = Selection(q, k, t, t, 25)
+    ambiguous = sel.check(lists, total)
+    clear = sorted((h, u) for h in range(16) for u in range(sel.exact.shape[1]) if (h, u) not in ambiguous)
+    g = np.random.default_rng(81)
+    picks = [clear[i] for i in sorted(g.choice(len(clear), min(6, len(clear)), replace=False))]
+    for h, u in picks:
+        rows_q = np.sort(g.choice(np.arange(u * UNIT, min(n, (u + 1) * UNIT)), 16, replace=False))
+        o_ref, l_ref, l_bnd = oracle_forward(q, k, v, t, t, SCALE, rows=rows_q, heads=[h],
+                                             tile_keep=sel.exact, unit_rows=UNIT, tile_keys=TILE)
+        check_o(host(o)[rows_q][:, [h]], o_ref, f"sparse pack, head {h} unit {u}")
+        check_lse(host(lse)[[h]][:, rows_q], l_ref, f"sparse pack, head {h} unit {u}", l_bnd)
