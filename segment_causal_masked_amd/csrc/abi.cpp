@@ -409,7 +409,7 @@ namespace {
 // 4096 entries) sort keys [H][pair_total] uint64] [partial slots], each part
 // 256-byte aligned.
 struct FwdWorkspace {
-  size_t lists = 0, k_sum = 0, q_sum = 0, keys = 0, partial = 0, total = 0;
+  size_t lists = 0, k_sum = 0, q_sum = 0, keys = 0, partial = 0, claim = 0, total = 0;
   bool has_keys = false;
 };
 
@@ -435,6 +435,10 @@ FwdWorkspace fwd_workspace(const nomas::HostPlan& h) {
   }
   w.partial = at;
   at += (size_t)h.n_slots * nomas::attn_fwd_slot_bytes();
+  if (h.n_chunks > 0) {  // the tail chunks' claim counter
+    w.claim = at;
+    at += 256;
+  }
   w.total = at;
   return w;
 }
@@ -543,6 +547,9 @@ nomas_status fwd_impl(const nomas_plan* p, const nomas_kvcache* cache, const voi
   fp.wg_ptr = p->d_wg_ptr;
   fp.pieces = p->d_pieces;
   fp.combine = p->d_combine;
+  fp.chunks = p->d_pieces + h.wg_ptr.back();
+  fp.n_chunks = h.n_chunks;
+  fp.claim = h.n_chunks > 0 ? reinterpret_cast<uint32_t*>(wsb + ws.claim) : nullptr;
   fp.unit_shift = p->d_unit_shift;
   fp.partial = reinterpret_cast<float*>(wsb + ws.partial);
   fp.groups = h.fwd_groups;

@@ -286,9 +286,24 @@ __global__ __launch_bounds__(NTHREADS, 1) __attribute__((amdgpu_waves_per_eu(2, 
   lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
   lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
 
-  for (int pc = pc0; pc < pc1; ++pc) {
-    const int unit = pieces[4 * pc];
-    const int e_begin = pieces[4 * pc + 1], e_end = pieces[4 * pc + 2], slot = pieces[4 * pc + 3];
+  // The workgroup's own pieces, then (long calls) tail chunks claimed in turn
+  // from the per-call counter until none is left.
+  __shared__ int s_claim;
+  const const_i32p chunk_list = (const_i32p)p.chunks;
+  for (int pc = pc0;; ++pc) {
+    const_i32p src;
+    if (pc < pc1) {
+      src = pieces + 4 * pc;
+    } else {
+      if (p.n_chunks == 0) break;
+      if (tid == 0) s_claim = (int)atomicAdd(p.claim, 1u);
+      lds_barrier();
+      const int c = __builtin_amdgcn_readfirstlane(s_claim);
+      if (c >= p.n_chunks) break;
+      src = chunk_list + 4 * c;
+    }
+    const int unit = src[0];
+    const int e_begin = src[1], e_end = src[2], slot = src[3];
     const int h = unit / p.n_pairs;
     const int pr = unit - h * p.n_pairs;
     const int qrow = pr * UNIT_ROWS + w * 32 + jq;
@@ -434,6 +449,12 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   store_row(p, acc, db, 1, m, l, h, qrow, hh, db == 0);
 }
 
+// Reset of the tail-chunk counter before a call (a kernel rather than a
+// memset, so that graph capture records a kernel node).
+__global__ __launch_bounds__(64) void attn_fwd_claim_reset_kernel(uint32_t* claim) {
+  if (threadIdx.x == 0) claim[threadIdx.x] = 0u;
+}
+
 }  // namespace
 
 size_t attn_fwd_slot_bytes() { return (size_t)SLOT_WORDS * sizeof(uint32_t); }
@@ -441,6 +462,11 @@ int attn_fwd_groups_per_cu() { return 1; }
 
 hipError_t launch_attn_fwd(const FwdParams& p, hipStream_t stream) {
   if (p.nq == 0) return hipSuccess;
+  if (p.n_chunks > 0) {  // the tail chunks are handed out from zero in every call
+    hipLaunchKernelGGL(attn_fwd_claim_reset_kernel, dim3(1), dim3(64), 0, stream, p.claim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)p.groups), dim3(NTHREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;

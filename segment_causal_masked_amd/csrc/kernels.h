@@ -31,13 +31,15 @@ struct FwdParams {
   const int32_t* wg_ptr;   // groups+1: pieces of each persistent workgroup
   const int4* pieces;      // {unit, entry_begin, entry_end, slot or -1}
   const int4* combine;     // {unit, first_slot, n_pieces, 0}
+  const int4* chunks;      // tail pieces, claimed in turn through *claim (or none)
+  uint32_t* claim;         // workspace: the next chunk to hand out (zeroed per call)
   const int32_t* unit_shift;  // per unit: entries visited in order (j + shift) mod n
   int64_t list_head_stride;    // lists per head (sparse plans), else 0: unit (h, u')
                                // walks csr_idx + h * list_head_stride + csr_ptr[u']
   float* partial;          // workspace: n_slots * attn_fwd_slot_bytes()
   int64_t q_stride, kv_stride, kv_head_stride, o_stride, cache_cap;
   int32_t nq, nk, n_cached, heads, nqt, nkt;
-  int32_t groups, n_combine, n_pairs;
+  int32_t groups, n_combine, n_pairs, n_chunks;
   float scale_log2;        // softmax scale * log2(e)
 };
 

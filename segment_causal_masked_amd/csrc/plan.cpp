@@ -520,11 +520,47 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     }
   }
 
-  // pieces: the units each range overlaps; a workgroup's time tau counts the
-  // iterations it has done before a piece
   std::vector<int64_t> ustart(size_t(n_units) + 1, 0);
   for (int64_t u = 0; u < n_units; ++u) ustart[size_t(u)] = unit_start(u);
   ustart[size_t(n_units)] = total;
+  auto unit_at = [&](int64_t i) {  // the unit holding iteration i
+    return int64_t(std::upper_bound(ustart.begin(), ustart.end() - 1, i) - ustart.begin()) - 1;
+  };
+
+  // Dynamic tail, for calls long enough to pay for it: the last
+  // TAIL_FRACTION of every workgroup's work is cut from the end of its last
+  // range into chunks of at most TAIL_CHUNK entries of one unit, which the
+  // workgroups claim in turn (an atomic counter per call) once their own
+  // ranges are done -- so that the workgroups that run faster (the XCDs of
+  // one chip differ by a few percent, and so do workgroups that share their
+  // key tiles in L2 with more or fewer others) take over the others' ends.
+  // Chunks are listed position by position across the workgroups, so that
+  // the first claims take the first chunk of every pool.
+  constexpr double TAIL_FRACTION = 0.05;
+  constexpr int64_t TAIL_CHUNK = 64, TAIL_MIN_WORK = 1024;
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> pool(static_cast<size_t>(groups));
+  if (groups > 0 && total / groups >= TAIL_MIN_WORK) {
+    for (int64_t g = 0; g < groups; ++g) {
+      auto& rs = ranges[size_t(g)];
+      if (rs.empty()) continue;
+      int64_t work = 0;
+      for (const auto& rg : rs) work += rg.second - rg.first;
+      auto& last = rs.back();
+      const int64_t take = std::min(last.second - last.first, int64_t(TAIL_FRACTION * double(work)));
+      const int64_t end = last.second;
+      last.second -= take;
+      for (int64_t i = last.second; i < end;) {
+        const int64_t u = unit_at(i);
+        const int64_t stop = std::min({end, ustart[size_t(u)] + unit_len(u), i + TAIL_CHUNK});
+        if (stop <= i) break;  // (a zero-length unit cannot hold an iteration)
+        pool[size_t(g)].push_back({i, stop});
+        i = stop;
+      }
+    }
+  }
+
+  // pieces: the units each range overlaps; a workgroup's time tau counts the
+  // iterations it has done before a piece
   std::vector<std::vector<Piece>> per(static_cast<size_t>(groups));
   std::vector<std::vector<int64_t>> tau(static_cast<size_t>(groups));
   std::vector<int32_t> n_pc(size_t(n_units), 0);
@@ -560,6 +596,19 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     tau[size_t(owner)].push_back(0);
     ++n_pc[size_t(u)];
   }
+  std::vector<Piece> chunks;
+  for (size_t pos = 0;; ++pos) {
+    bool any = false;
+    for (int64_t g = 0; g < groups; ++g) {
+      if (pos >= pool[size_t(g)].size()) continue;
+      any = true;
+      const auto& c = pool[size_t(g)][pos];
+      const int64_t u = unit_at(c.first), st = ustart[size_t(u)];
+      chunks.push_back(Piece{int32_t(u), int32_t(c.first - st), int32_t(c.second - st), -1});
+      ++n_pc[size_t(u)];
+    }
+    if (!any) break;
+  }
   // slots and merge items for split units (slots of a unit are consecutive)
   std::vector<int32_t> first_slot(size_t(n_units), -1), next_slot(size_t(n_units), 0);
   for (int64_t u = 0; u < n_units; ++u)
@@ -587,11 +636,15 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
         p.unit_shift[size_t(u)] = int32_t(shift);
       }
     }
+  for (Piece& pc : chunks)
+    if (first_slot[size_t(pc.unit)] >= 0) pc.slot = first_slot[size_t(pc.unit)] + next_slot[size_t(pc.unit)]++;
   p.wg_ptr.assign(size_t(groups) + 1, 0);
   for (int32_t g = 0; g < groups; ++g) {
     p.pieces.insert(p.pieces.end(), per[size_t(g)].begin(), per[size_t(g)].end());
     p.wg_ptr[size_t(g) + 1] = int32_t(p.pieces.size());
   }
+  p.n_chunks = int32_t(chunks.size());
+  p.pieces.insert(p.pieces.end(), chunks.begin(), chunks.end());
 }
 
 void build_bwd_schedule(HostPlan* pp) {
@@ -706,8 +759,9 @@ std::string validate_host_plan(const HostPlan& p) {
   if (int64_t(lptr.size()) != p.n_pairs + 1) return bad("list pointers of the schedule");
   // pieces: every unit's entries [0, n) covered exactly once; slots and merges
   const int64_t n_units = int64_t(p.heads) * p.n_pairs;
-  if (int64_t(p.wg_ptr.size()) != int64_t(p.fwd_groups) + 1 || p.wg_ptr[0] != 0 ||
-      p.wg_ptr.back() != int32_t(p.pieces.size()))
+  // (the pieces past the last workgroup's are the claimed tail chunks)
+  if (int64_t(p.wg_ptr.size()) != int64_t(p.fwd_groups) + 1 || p.wg_ptr[0] != 0 || p.n_chunks < 0 ||
+      int64_t(p.wg_ptr.back()) + p.n_chunks != int64_t(p.pieces.size()))
     return bad("workgroup pointers");
   for (int32_t g = 0; g < p.fwd_groups; ++g)
     if (p.wg_ptr[size_t(g + 1)] < p.wg_ptr[size_t(g)]) return bad("workgroup pointers not monotone");

@@ -76,7 +76,8 @@ struct HostPlan {
   std::vector<int32_t> pair_ptr, pair_idx;  // merged entry lists per q-tile pair
   int32_t fwd_groups = 0;
   std::vector<int32_t> wg_ptr;        // fwd_groups + 1
-  std::vector<Piece> pieces;
+  std::vector<Piece> pieces;          // per workgroup (wg_ptr), then the n_chunks
+  int32_t n_chunks = 0;               // tail chunks any workgroup claims in turn
   std::vector<CombineItem> combine;
   int32_t n_slots = 0;
   // per unit: its entries are visited in the rotated order
