@@ -284,6 +284,10 @@ nomas_status nomas_attn_fwd_noalloc(const nomas_plan* plan, const nomas_kvcache*
  * Backward (plans without a cache: training packs)
  * ------------------------------------------------------------------------ */
 
+/* Workspace of nomas_attn_bwd: two fp32 row statistics per head and padded
+ * query row, then 256 bytes of work-queue counters (never zero bytes).  A
+ * workspace serves one backward call at a time: calls that overlap on the
+ * device need one workspace each. */
 nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* plan, size_t* bytes);
 
 /* Gradients of O = attention(Q, K, V) for upstream dO:
@@ -293,8 +297,10 @@ nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* plan, size_t* bytes
  * exp(scale * (Q K^T) - lse) from Q and K as given and lse from
  * nomas_attn_fwd on the same inputs.  q, o, d_o, dq share q_stride; k, v, dk,
  * dv share kv_stride (elements).  dq, dk, dv are written (not accumulated):
- * bf16, or fp32 if the plan was built with NOMAS_PLAN_GRAD_F32.  The work is
- * deterministic (no atomics): equal inputs give bit-identical gradients.
+ * bf16, or fp32 if the plan was built with NOMAS_PLAN_GRAD_F32.  Workgroups
+ * claim their units (key-tile pairs, query-tile pairs) from counters in the
+ * workspace, but each unit is summed by one workgroup in a fixed order, with
+ * no atomic adds on values: equal inputs give bit-identical gradients.
  * Errors: INVALID_ARGUMENT (plan with a cache, host-only plan, missing
  * pointer or workspace), UNSUPPORTED (video-block sparse plan), ALIGNMENT,
  * HIP. */

@@ -612,8 +612,9 @@ nomas_status nomas_attn_fwd_noalloc(const nomas_plan* p, const nomas_kvcache* ca
 
 nomas_status nomas_attn_bwd_workspace_size(const nomas_plan* p, size_t* bytes) {
   if (!p || !bytes) return fail(NOMAS_ERR_INVALID_ARGUMENT, "NULL argument");
-  // -delta and -lse * log2(e) per (head, query row of the padded q-tiles)
-  *bytes = 2 * (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float);
+  // -delta and -lse * log2(e) per (head, query row of the padded q-tiles),
+  // then the two kernels' work-queue counters
+  *bytes = 2 * (size_t)p->host.heads * (size_t)p->host.nqt * 128 * sizeof(float) + 256;
   return ok();
 }
 
@@ -657,6 +658,8 @@ nomas_status nomas_attn_bwd(const nomas_plan* p, const void* q, const void* k, c
   bp.dv = static_cast<uint16_t*>(dv);
   bp.ndelta = static_cast<float*>(workspace);
   bp.nlse2 = bp.ndelta + (size_t)h.heads * (size_t)h.nqt * 128;
+  bp.claim = reinterpret_cast<uint32_t*>(bp.nlse2 + (size_t)h.heads * (size_t)h.nqt * 128);
+  bp.groups = std::max<int32_t>(1, h.fwd_groups);
   bp.qdesc = p->d_qdesc;
   bp.kdesc = p->d_kdesc;
   bp.pair_ptr = p->d_pair_ptr;

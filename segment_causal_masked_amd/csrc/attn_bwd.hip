@@ -22,10 +22,16 @@
 //      each q-tile), looping over the q-tiles that see those keys (the union
 //      of the two key tiles' column lists); 128-query tiles of Q, dO and the
 //      row statistics are staged in LDS, double buffered; dK and dV
-//      accumulate in registers and the two halves are summed at the end;
+//      accumulate in registers and the two halves are summed at the end.
+//      The grid has 1/16 more workgroups than units; each claims one unit
+//      from the work queues below and the surplus ones find none and exit
+//      (a loop over claimed units would hold more registers than the 256
+//      this kernel already uses, and it measured slower);
 //   3. bwd_dq_kernel: one workgroup per pair of 128-query tiles (eight waves,
 //      32 queries each) looping over the forward's key-tile lists, with K / V
-//      tiles staged as in the forward; dQ accumulates in registers.
+//      tiles staged as in the forward; dQ accumulates in registers.  One
+//      persistent workgroup per CU loops over units claimed from the work
+//      queues.
 // Only FULL / PARTIAL tiles are visited and the per-element mask is applied on
 // PARTIAL (or ragged) tiles only, as in the forward.
 //
@@ -49,14 +55,36 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Workgroup b is dispatched to XCD b % 8.  Map it to unit
-// (b % 8) * ceil(G / 8) + b / 8, so that each XCD works through a contiguous
-// range of units -- neighbouring tiles of the same head, whose Q / dO or K / V
-// tiles then meet in that XCD's L2 -- instead of every eighth unit.
-__device__ __forceinline__ int xcd_major_unit(int b, int G) {
-  const int per = (G + 7) >> 3;
-  const int u = (b & 7) * per + (b >> 3);
-  return u;
+// Work queues of the dK/dV and dQ kernels.  Workgroup b is dispatched to XCD
+// b % 8; the n_units units form n_q queues of consecutive units
+// ([q n / n_q, (q + 1) n / n_q)), one per XCD when the grid is a multiple of
+// 8.  A workgroup takes units from its own XCD's queue, so that each XCD works
+// through neighbouring tiles of one head, whose Q / dO or K / V tiles then
+// meet in its L2, and once that queue is drained from the others in turn:
+// the XCDs do not run at quite the same speed, and a fixed share per XCD
+// would leave the faster ones idle at the end.  Thread 0 claims (one atomic
+// add on the queue's counter; the counters are zeroed per call by the
+// row-statistics kernel) and broadcasts the unit through LDS; -1 when every
+// queue is drained.  `tried` (thread 0's) counts the queues found empty.
+__device__ __forceinline__ int claim_unit(uint32_t* ctr, int n_units, int& tried, int* slot) {
+  const int n_q = (gridDim.x & 7) ? 1 : 8;
+  if (threadIdx.x == 0) {
+    const int own = (int)(blockIdx.x & (unsigned)(n_q - 1));
+    int got = -1;
+    while (tried < n_q) {
+      const int q = (own + tried) & (n_q - 1);
+      const int b = (int)(((int64_t)q * n_units) / n_q), e = (int)(((int64_t)(q + 1) * n_units) / n_q);
+      const int i = (int)atomicAdd(ctr + q, 1u);
+      if (b + i < e) {
+        got = b + i;
+        break;
+      }
+      ++tried;
+    }
+    *slot = got;
+  }
+  lds_barrier();
+  return __builtin_amdgcn_readfirstlane(*slot);
 }
 
 // ---------------------------------------------------------------------------
@@ -70,6 +98,7 @@ __global__ __launch_bounds__(256) void bwd_rowstats_kernel(BwdParams p) {
   const int64_t rows = (int64_t)p.nqt * 128;
   const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int sub = threadIdx.x & 15;
+  if (blockIdx.x == 0 && threadIdx.x < 16) p.claim[threadIdx.x] = 0u;  // the queues start empty-handed
   if (item >= rows * p.heads) return;  // whole 16-lane groups leave together
   const int h = (int)(item / rows);
   const int i = (int)(item - (int64_t)h * rows);
@@ -297,14 +326,16 @@ __global__ __launch_bounds__(KV_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char stg0[KV_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stg1[KV_STAGE_BYTES];
   __shared__ int4 lane_bases[KV_THREADS];  // per-lane LDS read bases (see kv_qtile)
+  __shared__ int s_unit;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
   const int kg = w & 3, qh = w >> 2;
-  const int unit = xcd_major_unit(blockIdx.x, (int)gridDim.x);  // h * n_kpairs + u
-  if (unit >= p.heads * p.n_kpairs) return;
+  int tried = 0;
+  const int unit = claim_unit(p.claim, p.heads * p.n_kpairs, tried, &s_unit);  // h * n_kpairs + u
+  if (unit < 0) return;
   const int h = unit / p.n_kpairs;
   const int u = unit - h * p.n_kpairs;
   const int sub = kg >> 1;                     // which key tile of the pair
@@ -519,107 +550,116 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
   const int half = w >> 2;  // which q-tile of the pair
-  const int unit = xcd_major_unit(blockIdx.x, (int)gridDim.x);
-  if (unit >= p.heads * p.n_pairs) return;
-  const int h = unit / p.n_pairs;
-  const int pr = unit - h * p.n_pairs;
-  const int qrow = pr * 256 + w * 32 + jq;
-  const float scale_log2 = p.scale_log2;
+  __shared__ int s_unit;
 
-  QWave st;
-  float nl2, nd;  // -lse2 and -delta of this lane's query
-  {
-    const int qr = qrow < p.nq ? qrow : p.nq - 1;  // rows past nq: computed, never stored
-    const int64_t off = (int64_t)qr * p.q_stride + (int64_t)h * D + 8 * hh;
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      st.qf[s8] = *reinterpret_cast<const bf16x8*>(p.q + off + 16 * s8);
-      st.dof[s8] = *reinterpret_cast<const bf16x8*>(p.d_o + off + 16 * s8);
-    }
-    const bool in_tiles = qrow < p.nqt * QT_ROWS;
-    const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qrow;
-    nl2 = in_tiles ? p.nlse2[srow] : 0.f;
-    nd = in_tiles ? p.ndelta[srow] : 0.f;
-    st.qd = in_tiles ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
-    const int krow = kmap(jq), ksw = (krow >> 2) & 3;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) st.kbase[e] = krow * 64 + 16 * ((2 * e + hh) ^ ksw);
-    const int tr_j = (lane & 15) >> 2, tr_c4 = lane & 3;
-    const int x = 2 * ((lane >> 4) & 1) + (tr_c4 >> 1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      st.tbase[r] = (8 * hh + tr_j + 4 * r) * 64 + 16 * (x ^ (2 * hh + r)) + 8 * (tr_c4 & 1);
-  }
+  // persistent: one unit (h * n_pairs + pair) per claim until the queues run dry
+  const int n_units = p.heads * p.n_pairs;
+  int tried = 0;
+  for (;;) {
+    const int unit = claim_unit(p.claim + 8, n_units, tried, &s_unit);
+    if (unit < 0) break;
+    const int h = unit / p.n_pairs;
+    const int pr = unit - h * p.n_pairs;
+    const int qrow = pr * 256 + w * 32 + jq;
+    const float scale_log2 = p.scale_log2;
 
-  LoadCtx lc;
-  lc.kv_stride = p.kv_stride;
-  lc.nk = p.nk;
-  lc.n_cached = 0;
-  lc.lane_row = 16 * (w & 3) + (lane >> 2);
-  lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
-  lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
-  lc.k_cache_h = p.k;  // unused: no cached keys
-  lc.v_cache_h = p.v;
-  lc.k_new_h = p.k + (int64_t)h * p.kv_head_stride;
-  lc.v_new_h = p.v + (int64_t)h * p.kv_head_stride;
-
-  const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
-  const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
-  wait_vm_all();  // rows and statistics in registers before the tile loads start
-  st.nlse2 = nl2;
+    QWave st;
+    float nl2, nd;  // -lse2 and -delta of this lane's query
+    {
+      const int qr = qrow < p.nq ? qrow : p.nq - 1;  // rows past nq: computed, never stored
+      const int64_t off = (int64_t)qr * p.q_stride + (int64_t)h * D + 8 * hh;
 #pragma unroll
-  for (int ri = 0; ri < 16; ++ri) st.negdelta[ri] = nd;
-
-  // (always_inline: otherwise the wave state would be passed through scratch)
-  auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) __attribute__((always_inline)) {
-    issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
-    issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
-    if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
-  };
-  auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
-    if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
-    // one code path for FULL and PARTIAL tiles (a second variant would push
-    // the wave past its 256 registers); the per-element mask sits behind a
-    // uniform branch that FULL tiles skip
-    const bool masked = (here >> half) & 1;
-    const uint32_t vis = masked ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
-    dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, scale_log2, hh);
-  };
-  // four stages used as two pairs, one barrier per pair (as in the forward)
-  auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
-                  uint32_t n0, uint32_t nk0, uint32_t n1, uint32_t nk1) __attribute__((always_inline)) {
-    const int last = n_ent - 1;
-    const int e0 = ent[t], e1 = ent[min(t + 1, last)];
-    int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
-    // (pin the loads here: otherwise they are rematerialised after the barrier)
-    asm volatile("" : "+s"(e2), "+s"(e3));
-    wait_vm_all();
-    lds_barrier();
-    if (t + 2 < n_ent) issue_tile(e2 >> 4, n0, nk0);
-    if (t + 3 < n_ent) issue_tile(e3 >> 4, n1, nk1);
-    tile(e0, b0, k0);
-    if (t + 1 < n_ent) tile(e1, b1, k1);
-  };
-  if (n_ent > 0) issue_tile(ent[0] >> 4, lb0, lk0);
-  if (n_ent > 1) issue_tile(ent[1] >> 4, lb1, lk1);
-  for (int t = 0; t < n_ent; t += 4) {
-    pair(t, sbuf0, skd0, sbuf1, skd1, lb2, lk2, lb3, lk3);
-    if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, lb0, lk0, lb1, lk1);
-  }
-
-  if (qrow < p.nq) {
-    // a row that sees no key (padding) may have been computed unmasked on
-    // tiles no other row needs a mask for: its gradient is zero
-    if (st.qd.seg < 0) {
+      for (int s8 = 0; s8 < 8; ++s8) {
+        st.qf[s8] = *reinterpret_cast<const bf16x8*>(p.q + off + 16 * s8);
+        st.dof[s8] = *reinterpret_cast<const bf16x8*>(p.d_o + off + 16 * s8);
+      }
+      const bool in_tiles = qrow < p.nqt * QT_ROWS;
+      const int64_t srow = (int64_t)h * p.nqt * QT_ROWS + qrow;
+      nl2 = in_tiles ? p.nlse2[srow] : 0.f;
+      nd = in_tiles ? p.ndelta[srow] : 0.f;
+      st.qd = in_tiles ? p.qdesc[qrow] : QDescDev{-1, 0, 0u, 0};
 #pragma unroll
       for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
+      const int krow = kmap(jq), ksw = (krow >> 2) & 3;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) st.kbase[e] = krow * 64 + 16 * ((2 * e + hh) ^ ksw);
+      const int tr_j = (lane & 15) >> 2, tr_c4 = lane & 3;
+      const int x = 2 * ((lane >> 4) & 1) + (tr_c4 >> 1);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        st.tbase[r] = (8 * hh + tr_j + 4 * r) * 64 + 16 * (x ^ (2 * hh + r)) + 8 * (tr_c4 & 1);
     }
-    const int64_t off = (int64_t)qrow * p.q_stride + (int64_t)h * D;
-    if (p.grad_f32) store_grad_row<true>(p.dq, off, st.acc, p.scale, hh);
-    else store_grad_row<false>(p.dq, off, st.acc, p.scale, hh);
+
+    LoadCtx lc;
+    lc.kv_stride = p.kv_stride;
+    lc.nk = p.nk;
+    lc.n_cached = 0;
+    lc.lane_row = 16 * (w & 3) + (lane >> 2);
+    lc.lane_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    lc.lane_cache = (uint32_t)(lc.lane_row * D + 8 * lc.lane_chunk) * 2u;
+    lc.lane_new = (uint32_t)((int)(lc.lane_row * p.kv_stride) + 8 * lc.lane_chunk) * 2u;
+    lc.k_cache_h = p.k;  // unused: no cached keys
+    lc.v_cache_h = p.v;
+    lc.k_new_h = p.k + (int64_t)h * p.kv_head_stride;
+    lc.v_new_h = p.v + (int64_t)h * p.kv_head_stride;
+
+    const const_i32p ent = (const_i32p)p.pair_idx + ((const_i32p)p.pair_ptr)[pr];
+    const int n_ent = ((const_i32p)p.pair_ptr)[pr + 1] - ((const_i32p)p.pair_ptr)[pr];
+    wait_vm_all();  // rows and statistics in registers before the tile loads start
+    st.nlse2 = nl2;
+#pragma unroll
+    for (int ri = 0; ri < 16; ++ri) st.negdelta[ri] = nd;
+
+    // (always_inline: otherwise the wave state would be passed through scratch)
+    auto issue_tile = [&](int kt, uint32_t buf, uint32_t kd) __attribute__((always_inline)) {
+      issue_half(lc, lc.k_cache_h, lc.k_new_h, buf, kt, w);
+      issue_half(lc, lc.v_cache_h, lc.v_new_h, buf + TILE_BYTES, kt, w);
+      if (w == 0 && lane < 32) dma16_s(p.kdesc + kt * BK, 16u * lane, kd);
+    };
+    auto tile = [&](int here, const char* cbuf, const KDescDev* ckd) __attribute__((always_inline)) {
+      if ((here >> (2 + half)) & 1) return;  // EMPTY for this wave's q-tile
+      // one code path for FULL and PARTIAL tiles (a second variant would push
+      // the wave past its 256 registers); the per-element mask sits behind a
+      // uniform branch that FULL tiles skip
+      const bool masked = (here >> half) & 1;
+      const uint32_t vis = masked ? dq_vis_bits(st.qd, ckd, hh) : ~0u;
+      dq_tile(st, cbuf, cbuf + TILE_BYTES, masked, vis, scale_log2, hh);
+    };
+    // four stages used as two pairs, one barrier per pair (as in the forward)
+    auto pair = [&](int t, const char* b0, const KDescDev* k0, const char* b1, const KDescDev* k1,
+                    uint32_t n0, uint32_t nk0, uint32_t n1, uint32_t nk1) __attribute__((always_inline)) {
+      const int last = n_ent - 1;
+      const int e0 = ent[t], e1 = ent[min(t + 1, last)];
+      int e2 = ent[min(t + 2, last)], e3 = ent[min(t + 3, last)];
+      // (pin the loads here: otherwise they are rematerialised after the barrier)
+      asm volatile("" : "+s"(e2), "+s"(e3));
+      wait_vm_all();
+      lds_barrier();
+      if (t + 2 < n_ent) issue_tile(e2 >> 4, n0, nk0);
+      if (t + 3 < n_ent) issue_tile(e3 >> 4, n1, nk1);
+      tile(e0, b0, k0);
+      if (t + 1 < n_ent) tile(e1, b1, k1);
+    };
+    if (n_ent > 0) issue_tile(ent[0] >> 4, lb0, lk0);
+    if (n_ent > 1) issue_tile(ent[1] >> 4, lb1, lk1);
+    for (int t = 0; t < n_ent; t += 4) {
+      pair(t, sbuf0, skd0, sbuf1, skd1, lb2, lk2, lb3, lk3);
+      if (t + 2 < n_ent) pair(t + 2, sbuf2, skd2, sbuf3, skd3, lb0, lk0, lb1, lk1);
+    }
+
+    if (qrow < p.nq) {
+      // a row that sees no key (padding) may have been computed unmasked on
+      // tiles no other row needs a mask for: its gradient is zero
+      if (st.qd.seg < 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.acc[db] = f32x16{};
+      }
+      const int64_t off = (int64_t)qrow * p.q_stride + (int64_t)h * D;
+      if (p.grad_f32) store_grad_row<true>(p.dq, off, st.acc, p.scale, hh);
+      else store_grad_row<false>(p.dq, off, st.acc, p.scale, hh);
+    }
+    // (the next claim's barrier ends every wave's reads of the stage buffers
+    // before the next unit's loads refill them)
   }
 }
 
@@ -628,22 +668,24 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.heads <= 0) return hipSuccess;
   const int64_t items = (int64_t)p.heads * p.nqt * QT_ROWS * 16;
-  if (items > 0) {
-    hipLaunchKernelGGL(bwd_rowstats_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
-                       stream, p);
+  {  // at least one block: it also zeroes the work-queue counters
+    hipLaunchKernelGGL(bwd_rowstats_kernel, dim3((unsigned)std::max<int64_t>(1, (items + 255) / 256)),
+                       dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.nk > 0 && p.n_kpairs > 0) {
     const int units = p.heads * p.n_kpairs;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(8 * ((units + 7) / 8))), dim3(KV_THREADS),
+    // a surplus of 1/16: workgroups that a faster XCD runs after its own
+    // queue is drained take units from the others
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(8 * ((units + units / 16 + 7) / 8))), dim3(KV_THREADS),
                        0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.nq > 0 && p.n_pairs > 0) {
     const int units = p.heads * p.n_pairs;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)(8 * ((units + 7) / 8))), dim3(Q_THREADS), 0,
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)std::min(units, p.groups)), dim3(Q_THREADS), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

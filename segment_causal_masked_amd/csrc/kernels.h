@@ -117,6 +117,8 @@ struct BwdParams {
                            // fp32 elements when grad_f32 != 0, else bf16
   float* ndelta;           // workspace [H][nqt*128]: -rowsum(dO * O)
   float* nlse2;            // workspace [H][nqt*128]: -lse * log2(e), 0 where -inf or padding
+  uint32_t* claim;         // workspace: 8 + 8 work-queue counters of the dK/dV and dQ
+                           // kernels, zeroed by the row-statistics kernel
   const QDescDev* qdesc;   // nqt*128 entries
   const KDescDev* kdesc;   // nkt*64 entries
   const int32_t *pair_ptr, *pair_idx;    // per q-tile pair: the forward's key-tile lists
@@ -124,6 +126,7 @@ struct BwdParams {
   int64_t q_stride, kv_stride, kv_head_stride;  // k, v, dk, dv: row r of head h at
                                                 // r * kv_stride + h * kv_head_stride
   int32_t nq, nk, heads, nqt, nkt, n_pairs, n_kpairs;
+  int32_t groups;          // persistent workgroups of the dK/dV and dQ kernels (one per CU)
   int32_t grad_f32;
   float scale, scale_log2;
 };

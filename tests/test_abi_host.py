@@ -181,7 +181,8 @@ def test_host_only_plan_cannot_run_and_cache_checks():
 
 def test_backward_entry_checks_on_host_plans():
     """The backward refuses host-only plans and reports its workspace: two fp32
-    row statistics (-delta, -lse * log2 e) per head and padded query row."""
+    row statistics (-delta, -lse * log2 e) per head and padded query row, then
+    256 bytes of work-queue counters."""
     a = seg()
     b = seg(index=1)
     p = host_plan([a, b], [a, b], heads=3)
@@ -189,7 +190,7 @@ def test_backward_entry_checks_on_host_plans():
     n = C.c_size_t()
     assert lib.nomas_attn_bwd_workspace_size(p.handle, C.byref(n)) == 0
     nq = a.n_tokens + b.n_tokens
-    assert n.value == 2 * 3 * (-(-nq // 128) * 128) * 4
+    assert n.value == 2 * 3 * (-(-nq // 128) * 128) * 4 + 256
     fake = C.c_void_p(256)
     st = lib.nomas_attn_bwd(p.handle, fake, fake, fake, fake, fake, C.c_void_p(512), 3 * 128, 3 * 128,
                             fake, fake, fake, 0.1, fake, n.value, None)
