@@ -491,16 +491,36 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     const int64_t j = in <= 0.0 ? 0 : std::min<int64_t>(n, int64_t(std::llround(in / w_unit[size_t(u)])));
     return unit_start(u) + j;
   };
+  // Dynamic tail (below), for calls long enough to pay for it.
+  constexpr double TAIL_FRACTION = 0.05;
+  constexpr int64_t TAIL_CHUNK = 64, TAIL_MIN_WORK = 1024;
+  const bool dyn_tail = total / groups >= TAIL_MIN_WORK;
+  // Shares per XCD: the odd-numbered XCDs of the chip run about 3% slower
+  // than the even ones (per-workgroup timestamps on several machines; the
+  // slowness stays with the physical XCD when the work is handed out in the
+  // reverse XCD order), so without a dynamic tail to even them out their
+  // workgroups get a slightly smaller share of the cost (480p call -1.1%;
+  // with the tail, or with the phased schedule, skewed shares were slower).
+  constexpr double XCD_SKEW = 0.015;
+  const double skew = n_xcd == 8 && !phased && !dyn_tail ? XCD_SKEW : 0.0;
+  std::vector<double> xcd_at(size_t(n_xcd) + 1, 0.0);  // cumulative share, as a fraction
+  for (int32_t x = 0; x < n_xcd; ++x)
+    xcd_at[size_t(x + 1)] = xcd_at[size_t(x)] + 1.0 + (x % 2 ? -skew : skew);
+  for (auto& f : xcd_at) f /= xcd_at.back();
   std::vector<std::vector<std::pair<int64_t, int64_t>>> ranges(static_cast<size_t>(groups));
   if (!phased) {
     const double T = c_start.back();
+    auto at = [&](int64_t g) {  // cumulative share of workgroups 0 .. g - 1
+      const int64_t x = g / per_xcd, i = g - x * per_xcd;
+      return x >= n_xcd ? 1.0 : xcd_at[size_t(x)] + (xcd_at[size_t(x + 1)] - xcd_at[size_t(x)]) * double(i) / per_xcd;
+    };
     for (int64_t g = 0; g < groups; ++g)
-      ranges[size_t(g)].push_back({iter_at(T * double(g) / groups), iter_at(T * double(g + 1) / groups)});
+      ranges[size_t(g)].push_back({iter_at(T * at(g)), iter_at(T * at(g + 1))});
   } else {
     const double T = c_start.back();
     int64_t u = 0;
     for (int32_t x = 0; x < n_xcd; ++x) {
-      const int64_t s0 = iter_at(T * x / n_xcd), s1 = iter_at(T * (x + 1) / n_xcd);
+      const int64_t s0 = iter_at(T * xcd_at[size_t(x)]), s1 = iter_at(T * xcd_at[size_t(x + 1)]);
       int64_t a = s0;
       while (a < s1) {
         while (u < n_units && unit_start(u) + unit_len(u) <= a) ++u;
@@ -527,19 +547,17 @@ void build_fwd_schedule(HostPlan* pp, int32_t groups) {
     return int64_t(std::upper_bound(ustart.begin(), ustart.end() - 1, i) - ustart.begin()) - 1;
   };
 
-  // Dynamic tail, for calls long enough to pay for it: the last
-  // TAIL_FRACTION of every workgroup's work is cut from the end of its last
-  // range into chunks of at most TAIL_CHUNK entries of one unit, which the
-  // workgroups claim in turn (an atomic counter per call) once their own
-  // ranges are done -- so that the workgroups that run faster (the XCDs of
-  // one chip differ by a few percent, and so do workgroups that share their
-  // key tiles in L2 with more or fewer others) take over the others' ends.
-  // Chunks are listed position by position across the workgroups, so that
-  // the first claims take the first chunk of every pool.
-  constexpr double TAIL_FRACTION = 0.05;
-  constexpr int64_t TAIL_CHUNK = 64, TAIL_MIN_WORK = 1024;
+  // Dynamic tail: the last TAIL_FRACTION of every workgroup's work is cut
+  // from the end of its last range into chunks of at most TAIL_CHUNK entries
+  // of one unit, which the workgroups claim in turn (an atomic counter per
+  // call) once their own ranges are done -- so that the workgroups that run
+  // faster (the XCDs of one chip differ by a few percent, and so do
+  // workgroups that share their key tiles in L2 with more or fewer others)
+  // take over the others' ends.  Chunks are listed position by position
+  // across the workgroups, so that the first claims take the first chunk of
+  // every pool.
   std::vector<std::vector<std::pair<int64_t, int64_t>>> pool(static_cast<size_t>(groups));
-  if (groups > 0 && total / groups >= TAIL_MIN_WORK) {
+  if (dyn_tail) {
     for (int64_t g = 0; g < groups; ++g) {
       auto& rs = ranges[size_t(g)];
       if (rs.empty()) continue;
