@@ -111,9 +111,10 @@ def test_fp32_gradients_round_to_the_bf16_ones():
 
 
 def test_backward_repeats_bitwise():
-    """No atomics and a fixed schedule: two runs of the training-shape
-    backward on the same inputs give bit-identical gradients (a race between
-    waves or workgroups would show as a difference)."""
+    """Which workgroup takes which unit varies from run to run (work queues),
+    but each unit is summed by one workgroup in a fixed order: runs of the
+    training-shape backward on the same inputs give bit-identical gradients
+    (a race between waves or workgroups would show as a difference)."""
     need_gpu()
     w = wl.small_pack(5)
     segs = w.q_layout
@@ -128,6 +129,55 @@ def test_backward_repeats_bitwise():
         g2 = run_bwd(plan, q, k, v, o, d_o, lse, heads)
         for a, b, name in zip(g1, g2, ("dQ", "dK", "dV")):
             assert torch.equal(a, b), name
+
+
+def test_backward_degenerate_layouts_and_workspace_reuse():
+    """No queries (dK = dV = 0), no keys (dQ = 0) and a pack of padding only
+    (all three zero), all through one workspace; then a real pack through the
+    same workspace equals the same pack through a fresh one bit for bit (the
+    work-queue counters in the workspace are reset by every call)."""
+    need_gpu()
+    heads = 2
+    segs = wl.small_pack(2).q_layout
+    n = wl.layout_tokens(segs)
+    ws = torch.full((1 << 22,), 0xAB, dtype=torch.uint8, device="cuda")  # dirty on purpose
+
+    def bwd(plan, q, k, v, o, d_o, lse):
+        gs = [torch.full(x.shape, 7.0, dtype=torch.bfloat16, device="cuda") for x in (q, k, v)]
+        need = nm.nomas_attn_bwd_workspace_size(plan)
+        assert need <= ws.numel()
+        nm.nomas_attn_bwd(plan, q, k, v, o, d_o, lse, *gs, SCALE, workspace=ws[:need])
+        torch.cuda.synchronize()
+        return gs
+
+    k, v = (dev(wl.randn((n, heads, 128), 9300 + i)) for i in range(2))
+    # no queries
+    p0 = nm.nomas_attn_plan([], segs, heads=heads)
+    e = torch.empty((0, heads, 128), dtype=torch.bfloat16, device="cuda")
+    le = torch.empty((heads, 0), dtype=torch.float32, device="cuda")
+    _, dk, dv = bwd(p0, e, k, v, e, e, le)
+    assert (dk == 0).all() and (dv == 0).all()
+    # no keys: the queries see nothing
+    q, d_o = (dev(wl.randn((n, heads, 128), 9310 + i)) for i in range(2))
+    p1 = nm.nomas_attn_plan(segs, [], heads=heads)
+    o1, l1 = run_fwd(p1, None, q, e, e, heads)
+    assert (o1 == 0).all() and torch.isinf(l1).all()
+    dq, _, _ = bwd(p1, q, e, e, o1, d_o, l1)
+    assert (dq == 0).all()
+    # padding only
+    sp = [wl.Segment(0, 0, 0, 0, 0, [], n_pad=300)]
+    qp, kp, vp, dop = (dev(wl.randn((300, heads, 128), 9320 + i)) for i in range(4))
+    p2 = nm.nomas_attn_plan(sp, sp, heads=heads)
+    o2, l2 = run_fwd(p2, None, qp, kp, vp, heads)
+    for g in bwd(p2, qp, kp, vp, o2, dop, l2):
+        assert (g == 0).all()
+    # a real pack through the reused workspace and through a fresh one
+    p3 = nm.nomas_attn_plan(segs, segs, heads=heads)
+    o3, l3 = run_fwd(p3, None, q, k, v, heads)
+    g_reused = bwd(p3, q, k, v, o3, d_o, l3)
+    g_fresh = run_bwd(p3, q, k, v, o3, d_o, l3, heads)
+    for a, b, name in zip(g_reused, g_fresh, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b), name
 
 
 @pytest.mark.parametrize("mode", ["K", "H"])
