@@ -65,7 +65,11 @@ constexpr float LOG2E = 1.4426950408889634f;
 // would leave the faster ones idle at the end.  Thread 0 claims (one atomic
 // add on the queue's counter; the counters are zeroed per call by the
 // row-statistics kernel) and broadcasts the unit through LDS; -1 when every
-// queue is drained.  `tried` (thread 0's) counts the queues found empty.
+// queue is drained.  `tried` (thread 0's) counts the queues found empty.  A
+// loop of claims alternates between two slots: a unit without entries has no
+// barrier of its own, so a wave may still be about to read one claim's slot
+// when thread 0 writes the next claim; the claim after that waits at the
+// barrier for every wave.
 __device__ __forceinline__ int claim_unit(uint32_t* ctr, int n_units, int& tried, int* slot) {
   const int n_q = (gridDim.x & 7) ? 1 : 8;
   if (threadIdx.x == 0) {
@@ -550,13 +554,13 @@ __global__ __launch_bounds__(Q_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jq = lane & 31, hh = lane >> 5;
   const int half = w >> 2;  // which q-tile of the pair
-  __shared__ int s_unit;
+  __shared__ int s_unit[2];
 
   // persistent: one unit (h * n_pairs + pair) per claim until the queues run dry
   const int n_units = p.heads * p.n_pairs;
   int tried = 0;
-  for (;;) {
-    const int unit = claim_unit(p.claim + 8, n_units, tried, &s_unit);
+  for (int it = 0;; ++it) {
+    const int unit = claim_unit(p.claim + 8, n_units, tried, &s_unit[it & 1]);
     if (unit < 0) break;
     const int h = unit / p.n_pairs;
     const int pr = unit - h * p.n_pairs;

@@ -180,6 +180,17 @@ def test_backward_degenerate_layouts_and_workspace_reuse():
         assert torch.equal(a, b), name
 
 
+def test_pack_backward_with_padding_only_tile_pairs():
+    """640 padding tokens between the two videos of a pack: two query-tile
+    pairs see no key at all (units without entries in the dQ kernel's loop of
+    claims, between units with work), and the key tiles they would form are
+    seen by nobody; whole tensors against the oracle."""
+    need_gpu()
+    segs = wl.small_pack(3).q_layout
+    pad = wl.Segment(9, 0, 0, 0, 0, [], n_pad=640)
+    full_case(segs[:3] + [pad] + segs[3:], 2, 9400)
+
+
 @pytest.mark.parametrize("mode", ["K", "H"])
 def test_pack_backward_text_query_modes(mode):
     need_gpu()
