@@ -53,9 +53,19 @@ int main() {
         std::printf("status %d %s\n", st, err.c_str());
         continue;
       }
-      nomas::build_fwd_schedule(&plan, 256);
-      if (cached.empty()) nomas::build_bwd_schedule(&plan);
-      const std::string bad = nomas::validate_host_plan(plan);
+      // other device sizes too: a CU count that is a multiple of the 8 XCDs
+      // but not 256, and one that is not (per-XCD shares, phases and the
+      // tail depend on it); the printed line is the 256-workgroup plan's
+      std::string bad;
+      for (const int32_t groups : {120, 250, 256}) {
+        nomas::build_fwd_schedule(&plan, groups);
+        if (cached.empty()) nomas::build_bwd_schedule(&plan);
+        bad = nomas::validate_host_plan(plan);
+        if (!bad.empty()) {
+          bad += " (" + std::to_string(groups) + " workgroups)";
+          break;
+        }
+      }
       if (!bad.empty()) {
         std::printf("invalid %s\n", bad.c_str());
         ++failures;
